@@ -1,0 +1,185 @@
+/*
+ * pagedkv.h -- C ABI of the paged GQA attention library for AMD Instinct MI355X (gfx950).
+ *
+ * A continuously batched set of sequences keeps its keys and values in a
+ * shared pool of fixed-size blocks; each sequence owns a block table that
+ * maps its logical block i to a physical block of the pool.  Sources (web
+ * pages, cited by title and section):
+ *
+ *   [TGI]   "Text Generation Inference: Hugging Face's production-grade LLM
+ *           inference server" -- "The Investigation" (Finding 2: logical blocks
+ *           mapped to physical blocks through a per-sequence block table),
+ *           "Under the Hood: PagedAttention" (block table, shared pool, append
+ *           of a new token's K/V, gather of K/V tiles through the table),
+ *           "Under the Hood: Flash Attention" (exact softmax attention computed
+ *           tile by tile with a running max and sum), "Advanced Pattern:
+ *           Chunked Prefill" (prompt chunks interleaved with decode rows),
+ *           "Production Pattern: KV Cache Math" (bytes per token).
+ *   [SPEED] "How to Speed Up LLM Inference: KV Cache to Production Serving" --
+ *           "The KV cache: the memory problem that runs the show" (16-token
+ *           blocks, GQA, bytes-per-token formula).
+ *   [LIFE]  "The inference request lifecycle" -- "KV cache grows with the sum
+ *           of cached tokens" (formula; GQA shares K/V heads).
+ *   [V3]    pyshine walkthrough of text-generation-inference v3 -- "Inside the
+ *           batching task" (every forward has at least one fresh position),
+ *           "On the wire" paragraph of "The radix prefix cache" (the scheduler
+ *           ships block tables, not KV payloads).
+ *
+ * Common conventions
+ *   bf16      IEEE-754 binary16 "brain float" bit patterns, 2 bytes each.
+ *   Pools     k_cache and v_cache are separate device arrays of shape
+ *             [num_blocks, block_size, num_kv_heads, head_dim], bf16, dense
+ *             row-major.  A slot is block * block_size + offset; slot s's
+ *             head-h row starts at element (s * num_kv_heads + h) * head_dim.
+ *   GQA       num_q_heads is a multiple of num_kv_heads; query head g reads
+ *             KV head g / (num_q_heads / num_kv_heads) (contiguous groups).
+ *   Pointers  Arguments marked "device" are device pointers (hipMalloc'd or
+ *             equivalent) on the current HIP device; all other arguments are
+ *             host values.  The caller owns every buffer; the library never
+ *             allocates or frees device memory, never synchronises the
+ *             stream and never copies device data to the host.
+ *   Streams   `stream` is a hipStream_t (NULL = the null stream).  Work is
+ *             enqueued in call order; returning PKV_OK means enqueued, not
+ *             finished.
+ *   Errors    Argument checks run on the host before any HIP call.  On any
+ *             error nothing is enqueued.  Device-side metadata (slots, table
+ *             entries, lengths) is the caller's contract: kernels clamp or
+ *             skip out-of-range entries instead of touching memory outside
+ *             the pools, but the results for such inputs are unspecified.
+ */
+#ifndef PAGEDKV_H_
+#define PAGEDKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define PKV_API __attribute__((visibility("default")))
+#else
+#define PKV_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define PKV_OK            0   /* enqueued (or nothing to do)                        */
+#define PKV_EINVAL       (-1) /* null pointer, negative size, inconsistent shapes  */
+#define PKV_EUNSUPPORTED (-2) /* a shape the kernels are not built for             */
+#define PKV_EWORKSPACE   (-3) /* workspace too small (see paged_attention)         */
+#define PKV_EHIP         (-4) /* a HIP launch reported an error                    */
+
+/*
+ * kv_bytes_per_token -- bytes of K plus V that one token occupies in the cache.
+ *
+ * [TGI] "Production Pattern: KV Cache Math", [SPEED] "The KV cache..." and
+ * [LIFE] "KV cache grows with the sum of cached tokens": 2 (one K, one V) x
+ * layers x KV heads x head dim x bytes per element.  Pure host integer
+ * arithmetic in 64 bits; no HIP call.
+ *
+ * Returns the byte count, or -1 if any argument is <= 0 or the product does
+ * not fit in int64.
+ */
+PKV_API int64_t kv_bytes_per_token(int64_t num_layers, int64_t num_kv_heads, int64_t head_dim,
+                           int64_t dtype_bytes);
+
+/*
+ * kv_append -- scatter this step's new K and V rows into their pool slots.
+ *
+ * [TGI] "Under the Hood: PagedAttention": a generated token's K/V pair is
+ * appended at its sequence's next position, in the physical block the block
+ * table maps that position to (the caller computes slot_mapping from the
+ * tables).  For every i < num_tokens with slot_mapping[i] >= 0:
+ *     k_cache row (slot_mapping[i], h) = k_new row (i, h)   for every KV head h
+ *     v_cache row (slot_mapping[i], h) = v_new row (i, h)
+ * as an exact copy of the bf16 bits.  slot_mapping[i] < 0 marks a padding row
+ * and is skipped; a slot >= num_blocks * block_size is skipped as well
+ * (caller error; never written).
+ *
+ *   k_new, v_new   device, bf16 [num_tokens, num_kv_heads, head_dim], read only.
+ *   slot_mapping   device, int64 [num_tokens].
+ *   num_tokens     >= 0; 0 enqueues nothing and returns PKV_OK.
+ *   k_cache, v_cache  device, bf16 pools (see conventions), written in place.
+ *   num_blocks, block_size, num_kv_heads, head_dim   pool shape; > 0.
+ *   head_dim       a multiple of 8 (16-byte rows chunks); 64 and 128 are tuned.
+ *   stream         hipStream_t.
+ *
+ * Contract: slots are unique within one call (otherwise which row lands is
+ * unspecified) and do not target a block mapped by several sequences
+ * (shared prefix blocks are copied before a write, [TGI] "Prefix sharing").
+ * Enqueue the append before the attention call that reads those tokens.
+ * Returns PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED or PKV_EHIP.
+ */
+PKV_API int kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+              int64_t num_tokens, void* k_cache, void* v_cache, int64_t num_blocks,
+              int32_t block_size, int32_t num_kv_heads, int32_t head_dim, void* stream);
+
+/*
+ * paged_attention -- causal GQA attention of a mixed batch of decode rows and
+ * chunked-prefill rows over the paged cache.
+ *
+ * Sequence s has seq_lens[s] = L tokens (this step's appended tokens
+ * included) and q_s = query_start_loc[s+1] - query_start_loc[s] query rows,
+ * which are its last q_s tokens ([TGI] "Advanced Pattern: Chunked Prefill":
+ * a chunk continues an already-cached prefix; a decode row is q_s = 1).  Row
+ * j of s (global row query_start_loc[s] + j) sits at position p = L - q_s + j
+ * and, for every query head g, computes
+ *     out[row, g, :] = sum_{t<=p} softmax_t(scale * <q[row, g, :], K_t>) V_t
+ * where K_t, V_t are the rows of KV head g / (Hq/Hkv) at position t, found at
+ * block block_tables[s, t / block_size], offset t % block_size
+ * ([TGI] "Under the Hood: PagedAttention" / "Under the Hood: Flash
+ * Attention": exact softmax attention, never materialising the score matrix).
+ * Decode rows use split-K with a log-sum-exp merge; prefill rows use bf16
+ * matrix-core products with fp32 accumulation.  out is rounded to bf16
+ * (nearest-even).  Positions >= L and unreferenced blocks are never read into
+ * the result (they may hold any bits, NaN included).
+ *
+ *   out            device, bf16 [num_q_tokens, num_q_heads, head_dim], written.
+ *   q              device, bf16 [num_q_tokens, num_q_heads, head_dim].
+ *   k_cache, v_cache  device, bf16 pools.
+ *   block_tables   device, int32 [num_seqs, max_blocks_per_seq]; entries for
+ *                  logical blocks >= ceil(L / block_size) are never read.
+ *   seq_lens       device, int32 [num_seqs].
+ *   query_start_loc device, int32 [num_seqs + 1], non-decreasing,
+ *                  [0] = 0, [num_seqs] = num_q_tokens.
+ *   num_seqs, num_q_tokens   >= 0 (0 enqueues nothing).
+ *   max_blocks_per_seq  row length of block_tables; also bounds L:
+ *                  every L <= max_blocks_per_seq * block_size.
+ *   max_query_len  >= every q_s (host-side bound; sizes the prefill grid).
+ *   num_q_heads, num_kv_heads   Hq % Hkv == 0 and Hq/Hkv in {1,2,4,8,16}.
+ *   head_dim       64 or 128.
+ *   num_blocks, block_size   pool shape; block_size in {8, 16, 32}.
+ *   scale          softmax scale applied to <q, k> (e.g. 1/sqrt(head_dim)).
+ *   workspace      device scratch for split-K partials, or NULL.
+ *   workspace_bytes  in/out.  If workspace == NULL, the required size is
+ *                  written to *workspace_bytes and nothing is enqueued.
+ *                  Otherwise *workspace_bytes is the size of the buffer the
+ *                  caller passes (PKV_EWORKSPACE if smaller than required).
+ *                  The size depends only on num_seqs, num_q_heads, head_dim,
+ *                  max_blocks_per_seq and block_size.  The buffer needs no
+ *                  initialisation and must not be shared by calls that can
+ *                  run concurrently.
+ *   stream         hipStream_t.
+ *
+ * Contract: 1 <= q_s <= L for every sequence with rows (q_s = 0 is allowed
+ * and produces nothing); rows of different sequences may appear in any
+ * order.  Returns PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE or
+ * PKV_EHIP.
+ */
+PKV_API int paged_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* seq_lens,
+                    const int32_t* query_start_loc, int32_t num_seqs, int64_t num_q_tokens,
+                    int32_t max_blocks_per_seq, int32_t max_query_len, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                    int32_t block_size, float scale, void* workspace, size_t* workspace_bytes,
+                    void* stream);
+
+/* Human-readable name of a status code (static string). */
+PKV_API const char* pkv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H_ */

@@ -1,0 +1,17 @@
+"""Paged GQA attention over block tables for AMD Instinct MI355X (gfx950).
+
+The work is done by the HIP library ``libpagedkv.so`` (C ABI in
+``include/pagedkv.h``); this package is a thin ctypes binding with the same
+three calls, taking torch tensors for device memory and streams.  Importing
+the package does not load the library; the first call does, and fails loudly
+if it is missing (build it with ``python -m paged_kv_cache_tables_amd.build``).
+"""
+from ._lib import (  # noqa: F401
+    PagedKVError,
+    kv_append,
+    kv_bytes_per_token,
+    library_path,
+    load_library,
+    paged_attention,
+    workspace_bytes,
+)

@@ -1,0 +1,145 @@
+// C ABI of the library (declared in include/pagedkv.h): host-side argument
+// checks, workspace sizing and kernel dispatch.  No HIP call is made before
+// every argument has been validated.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "kernels.h"
+#include "pagedkv.h"
+
+namespace {
+
+constexpr int kSplitTokens = 512;   // split-K size of decode rows (a multiple of 64)
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct WsLayout {
+  int max_splits;
+  size_t o_off, m_off, l_off, total;
+};
+
+WsLayout workspace_layout(int num_seqs, int Hq, int D, int max_blocks, int bs) {
+  WsLayout w{};
+  const int64_t max_tokens = (int64_t)max_blocks * bs;
+  w.max_splits = (int)((max_tokens + kSplitTokens - 1) / kSplitTokens);
+  if (w.max_splits < 1) w.max_splits = 1;
+  const size_t cells = (size_t)num_seqs * Hq * w.max_splits;
+  w.o_off = 0;
+  w.m_off = round_up(cells * D * sizeof(float), 256);
+  w.l_off = w.m_off + round_up(cells * sizeof(float), 256);
+  w.total = w.l_off + round_up(cells * sizeof(float), 256);
+  if (w.total == 0) w.total = 256;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t kv_bytes_per_token(int64_t num_layers, int64_t num_kv_heads, int64_t head_dim,
+                           int64_t dtype_bytes) {
+  if (num_layers <= 0 || num_kv_heads <= 0 || head_dim <= 0 || dtype_bytes <= 0) return -1;
+  int64_t r = 2;
+  const int64_t f[4] = {num_layers, num_kv_heads, head_dim, dtype_bytes};
+  for (int i = 0; i < 4; ++i) {
+    if (r > INT64_MAX / f[i]) return -1;
+    r *= f[i];
+  }
+  return r;
+}
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_EINVAL: return "invalid argument";
+    case PKV_EUNSUPPORTED: return "unsupported shape";
+    case PKV_EWORKSPACE: return "workspace too small";
+    case PKV_EHIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+int kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping, int64_t num_tokens,
+              void* k_cache, void* v_cache, int64_t num_blocks, int32_t block_size,
+              int32_t num_kv_heads, int32_t head_dim, void* stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return PKV_EINVAL;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PKV_EINVAL;
+  if (head_dim % 8 != 0) return PKV_EUNSUPPORTED;   // rows move in 16-byte chunks
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(slot_mapping, 8))
+    return PKV_EINVAL;
+  if (num_blocks > INT64_MAX / block_size) return PKV_EINVAL;
+  if (num_tokens == 0) return PKV_OK;
+  const int row_chunks = num_kv_heads * head_dim / 8;
+  hipError_t e = pkv::launch_append(k_new, v_new, slot_mapping, num_tokens, k_cache, v_cache,
+                                    num_blocks * block_size, row_chunks, (hipStream_t)stream);
+  return e == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+int paged_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* seq_lens,
+                    const int32_t* query_start_loc, int32_t num_seqs, int64_t num_q_tokens,
+                    int32_t max_blocks_per_seq, int32_t max_query_len, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, int32_t block_size,
+                    float scale, void* workspace, size_t* workspace_bytes, void* stream) {
+  if (!workspace_bytes) return PKV_EINVAL;
+  if (num_seqs < 0 || num_q_tokens < 0 || max_blocks_per_seq < 1 || max_query_len < 0 ||
+      num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0 || block_size <= 0)
+    return PKV_EINVAL;
+  if (num_q_heads % num_kv_heads != 0) return PKV_EINVAL;
+  if (!isfinite(scale)) return PKV_EINVAL;
+  const int G = num_q_heads / num_kv_heads;
+  if (!pkv::decode_supported(head_dim, G, block_size) || !pkv::prefill_supported(head_dim, G, block_size))
+    return PKV_EUNSUPPORTED;
+  if (num_seqs > 65535 || num_q_heads > 65535) return PKV_EUNSUPPORTED;   // grid y/z limits
+  const WsLayout ws = workspace_layout(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size);
+  if (!workspace) {
+    *workspace_bytes = ws.total;
+    return PKV_OK;
+  }
+  if (*workspace_bytes < ws.total) return PKV_EWORKSPACE;
+  if (!aligned(workspace, 256)) return PKV_EINVAL;
+  if (num_seqs == 0 || num_q_tokens == 0) return PKV_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !seq_lens || !query_start_loc)
+    return PKV_EINVAL;
+  if (max_query_len < 1) return PKV_EINVAL;   // rows exist, so some sequence has q_s >= 1
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return PKV_EINVAL;
+
+  pkv::AttnParams p{};
+  p.out = (uint16_t*)out;
+  p.q = (const uint16_t*)q;
+  p.k_cache = (const uint16_t*)k_cache;
+  p.v_cache = (const uint16_t*)v_cache;
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.qsl = query_start_loc;
+  p.num_seqs = num_seqs;
+  p.num_q_tokens = num_q_tokens;
+  p.num_blocks = num_blocks;
+  p.max_blocks = max_blocks_per_seq;
+  p.max_query_len = max_query_len;
+  p.Hq = num_q_heads;
+  p.Hkv = num_kv_heads;
+  p.D = head_dim;
+  p.bs = block_size;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.split_tokens = kSplitTokens;
+  p.max_splits = ws.max_splits;
+  char* wsb = (char*)workspace;
+  p.ws_o = (float*)(wsb + ws.o_off);
+  p.ws_m = (float*)(wsb + ws.m_off);
+  p.ws_l = (float*)(wsb + ws.l_off);
+
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = pkv::launch_decode(p, st);
+  if (e == hipSuccess) e = pkv::launch_merge(p, st);
+  if (e == hipSuccess && max_query_len > 1) e = pkv::launch_prefill(p, st);
+  return e == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+}  // extern "C"

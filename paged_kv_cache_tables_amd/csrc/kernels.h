@@ -1,0 +1,43 @@
+// Launchers of the gfx950 kernels (internal to the library; the public ABI is include/pagedkv.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Everything one attention call needs on the device, passed by value to the kernels.
+struct AttnParams {
+  uint16_t* out;                  // bf16 [num_q_tokens, Hq, D]
+  const uint16_t* q;              // bf16 [num_q_tokens, Hq, D]
+  const uint16_t* k_cache;        // bf16 [num_blocks, bs, Hkv, D]
+  const uint16_t* v_cache;
+  const int32_t* block_tables;    // [num_seqs, max_blocks]
+  const int32_t* seq_lens;        // [num_seqs]
+  const int32_t* qsl;             // [num_seqs + 1]
+  int num_seqs;
+  int64_t num_q_tokens;
+  int64_t num_blocks;             // pool blocks: table entries outside [0, num_blocks) are skipped
+  int max_blocks;
+  int max_query_len;
+  int Hq, Hkv, D, bs;
+  float scale_log2;               // softmax scale * log2(e): scores live in the exp2 domain
+  int split_tokens;               // split-K size of decode rows (multiple of 64)
+  int max_splits;                 // ceil(max_blocks * bs / split_tokens)
+  float* ws_o;                    // [num_seqs, Hq, max_splits, D]  unnormalised partial outputs
+  float* ws_m;                    // [num_seqs, Hq, max_splits]     partial max (exp2 domain)
+  float* ws_l;                    // [num_seqs, Hq, max_splits]     partial sum of exponentials
+};
+
+hipError_t launch_append(const void* k_new, const void* v_new, const int64_t* slots, int64_t num_tokens,
+                         void* k_cache, void* v_cache, int64_t num_slots, int row_chunks,
+                         hipStream_t stream);
+
+bool decode_supported(int D, int G, int bs);
+hipError_t launch_decode(const AttnParams& p, hipStream_t stream);
+hipError_t launch_merge(const AttnParams& p, hipStream_t stream);
+
+bool prefill_supported(int D, int G, int bs);
+hipError_t launch_prefill(const AttnParams& p, hipStream_t stream);
+
+}  // namespace pkv

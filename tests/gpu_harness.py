@@ -1,0 +1,94 @@
+"""Helpers shared by the GPU tests: upload a seeded workload, run the library
+through its binding, compare with the CPU oracle under the stated tolerance."""
+from __future__ import annotations
+
+import numpy as np
+
+TOL_MAX_ABS = 1e-2      # per element, raised to one bf16 ulp of the reference where that is larger
+TOL_MEAN_ABS = 1e-3
+
+
+def to_dev(arr: np.ndarray, dtype, device="cuda:0"):
+    import torch
+    if dtype == torch.bfloat16:
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr))
+    return t.to(device)
+
+
+def to_host_bits(t) -> np.ndarray:
+    import torch
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+class DeviceBatch:
+    """Device copies of a workload's inputs (pools before the append)."""
+
+    def __init__(self, wl, device="cuda:0"):
+        import torch
+        self.wl = wl
+        self.q = to_dev(wl.q, torch.bfloat16, device)
+        self.k_new = to_dev(wl.k_new, torch.bfloat16, device)
+        self.v_new = to_dev(wl.v_new, torch.bfloat16, device)
+        self.slots = to_dev(wl.slot_mapping.astype(np.int64), torch.int64, device)
+        self.k_cache = to_dev(wl.k_cache, torch.bfloat16, device)
+        self.v_cache = to_dev(wl.v_cache, torch.bfloat16, device)
+        self.bt = to_dev(wl.block_tables.astype(np.int32), torch.int32, device)
+        self.seq_lens = to_dev(wl.seq_lens.astype(np.int32), torch.int32, device)
+        self.qsl = to_dev(wl.query_start_loc.astype(np.int32), torch.int32, device)
+        self.out = torch.empty_like(self.q)
+
+    def append(self):
+        import paged_kv_cache_tables_amd as pkv
+        pkv.kv_append(self.k_new, self.v_new, self.slots, self.k_cache, self.v_cache)
+
+    def attend(self, workspace=None):
+        import paged_kv_cache_tables_amd as pkv
+        pkv.paged_attention(self.out, self.q, self.k_cache, self.v_cache, self.bt, self.seq_lens, self.qsl,
+                            self.wl.scale, self.wl.max_query_len, workspace=workspace)
+
+    def step(self):
+        self.append()
+        self.attend()
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 numbers at |x| (8 significant bits)."""
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    return np.where(ax > 0, np.exp2(e - 7), 2.0 ** -133)
+
+
+def compare(out_bits: np.ndarray, ref: np.ndarray, rows=None, label=""):
+    """Assert parity; return the error statistics.  `rows`: global rows to check (None = all)."""
+    if rows is not None:
+        rows = np.asarray(sorted(rows))
+        out_bits = out_bits[rows]
+        ref = ref[rows]
+    got = bf16_to_f64(out_bits)
+    assert np.isfinite(ref).all(), "reference has NaN in the checked rows"
+    err = np.abs(got - ref)
+    floor = np.abs(ref - bf16_to_f64(_rne(ref)))
+    allowed = np.maximum(TOL_MAX_ABS, bf16_ulp(ref))
+    stats = dict(label=label, n=int(err.size), max_abs=float(err.max()), mean_abs=float(err.mean()),
+                 rounding_floor_max=float(floor.max()), n_ref_ge_4=int((np.abs(ref) >= 4).sum()),
+                 nonfinite=int((~np.isfinite(got)).sum()))
+    print("parity", stats, flush=True)
+    assert stats["nonfinite"] == 0, stats
+    bad = err > allowed
+    assert not bad.any(), (stats, np.argwhere(bad)[:5])
+    assert stats["mean_abs"] <= TOL_MEAN_ABS, stats
+    return stats
+
+
+def _rne(x: np.ndarray) -> np.ndarray:
+    """float64 -> nearest bf16 bits (via float32 first; exact for values already near bf16)."""
+    f = np.asarray(x, np.float32)
+    u = f.view(np.uint32)
+    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    return r.astype(np.uint16)

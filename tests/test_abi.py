@@ -1,0 +1,136 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+symbol, computes the byte formula, and rejects bad arguments on the host
+before any HIP call (each case below fails validation, so no kernel runs)."""
+import ctypes
+import json
+import os
+import re
+import subprocess
+
+import pytest
+
+import paged_kv_cache_tables_amd as pkv
+from paged_kv_cache_tables_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedkv.h")
+
+PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE = 0, -1, -2, -3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pkv.library_path()):
+        pytest.fail("libpagedkv.so is not built (python -m paged_kv_cache_tables_amd.build)")
+    return pkv.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"PKV_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("kv_append", "paged_attention", "kv_bytes_per_token"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", pkv.library_path()], capture_output=True, text=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_kv_bytes_per_token_golden(lib, golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "kv_bytes_per_token.json")))
+    for case in g["per_token"]:
+        assert lib.kv_bytes_per_token(*case["args"]) == case["expected"], case["cite"]
+    for bad in [(0, 8, 128, 2), (80, -8, 128, 2), (80, 8, 0, 2), (80, 8, 128, -1), (2 ** 62, 8, 128, 2)]:
+        assert lib.kv_bytes_per_token(*bad) == -1
+
+
+FAKE = 0x10000   # aligned, never dereferenced: every call below fails validation first
+
+
+def append_args(**over):
+    a = dict(k_new=FAKE, v_new=FAKE, slot_mapping=FAKE, num_tokens=4, k_cache=FAKE, v_cache=FAKE,
+             num_blocks=8, block_size=16, num_kv_heads=2, head_dim=64, stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(k_new=None), PKV_EINVAL),
+    (dict(slot_mapping=None), PKV_EINVAL),
+    (dict(num_tokens=-1), PKV_EINVAL),
+    (dict(num_blocks=0), PKV_EINVAL),
+    (dict(block_size=0), PKV_EINVAL),
+    (dict(head_dim=60), PKV_EUNSUPPORTED),
+    (dict(k_cache=FAKE + 8), PKV_EINVAL),          # not 16-byte aligned
+    (dict(num_tokens=0), PKV_OK),                   # nothing to do, nothing launched
+])
+def test_kv_append_validation(lib, over, expect):
+    assert lib.kv_append(*append_args(**over)) == expect
+
+
+def attn_args(**over):
+    n = ctypes.c_size_t(1 << 30)
+    a = dict(out=FAKE, q=FAKE, k_cache=FAKE, v_cache=FAKE, block_tables=FAKE, seq_lens=FAKE,
+             qsl=FAKE, num_seqs=4, num_q_tokens=8, max_blocks=4, max_query_len=5, Hq=4, Hkv=2, D=64,
+             num_blocks=64, bs=16, scale=0.125, workspace=None, workspace_bytes=ctypes.byref(n),
+             stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+def test_workspace_query_and_size(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.paged_attention(*attn_args(workspace_bytes=ctypes.byref(n))) == PKV_OK
+    # 4 seqs x 4 heads x 1 split x (64 + 2) floats, each array 256-byte aligned
+    assert n.value >= 4 * 4 * 1 * 66 * 4
+    small = ctypes.c_size_t(n.value - 1)
+    assert lib.paged_attention(*attn_args(workspace=FAKE, workspace_bytes=ctypes.byref(small))) == PKV_EWORKSPACE
+    assert pkv.workspace_bytes(4, 4, 2, 64, 4, 16) == n.value
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(workspace_bytes=None), PKV_EINVAL),
+    (dict(Hq=6, Hkv=4), PKV_EINVAL),               # not a multiple
+    (dict(Hq=32, Hkv=1), PKV_EUNSUPPORTED),        # group of 32 not built
+    (dict(D=96), PKV_EUNSUPPORTED),
+    (dict(bs=12), PKV_EUNSUPPORTED),
+    (dict(num_seqs=-1), PKV_EINVAL),
+    (dict(max_blocks=0), PKV_EINVAL),
+    (dict(scale=float("nan")), PKV_EINVAL),
+    (dict(num_blocks=0), PKV_EINVAL),
+])
+def test_paged_attention_validation(lib, over, expect):
+    assert lib.paged_attention(*attn_args(**over)) == expect
+
+
+def test_paged_attention_checks_pointers_before_launch(lib):
+    n = ctypes.c_size_t(1 << 30)
+    for field in ("out", "q", "k_cache", "v_cache", "block_tables", "seq_lens", "qsl"):
+        args = attn_args(workspace=FAKE, workspace_bytes=ctypes.byref(n), **{field: None})
+        assert lib.paged_attention(*args) == PKV_EINVAL, field
+    args = attn_args(workspace=FAKE + 16, workspace_bytes=ctypes.byref(n))
+    assert lib.paged_attention(*args) == PKV_EINVAL                     # workspace alignment
+    args = attn_args(workspace=FAKE, workspace_bytes=ctypes.byref(n), max_query_len=0)
+    assert lib.paged_attention(*args) == PKV_EINVAL                     # rows but no bound
+    args = attn_args(workspace=FAKE, workspace_bytes=ctypes.byref(n), num_q_tokens=0)
+    assert lib.paged_attention(*args) == PKV_OK                         # empty batch: no launch
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4):
+        assert lib.pkv_status_string(code).decode() == _lib.STATUS[code]
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "PKG", str(tmp_path))
+    with pytest.raises(FileNotFoundError):
+        _lib.kv_bytes_per_token(1, 1, 1, 1)

@@ -1,0 +1,258 @@
+"""GPU parity: the HIP library (through the C ABI) against the float64 CPU oracle.
+
+Bars: kv_append is bit-exact over the whole pool; attention is within
+1e-2 max abs (raised to one bf16 ulp of the reference where the bf16 output
+itself cannot resolve 1e-2, i.e. |ref| >= 2) and 1e-3 mean abs.  Large
+batches are checked on sampled rows, which the oracle computes one by one
+from the same inputs.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_harness import DeviceBatch, bf16_to_f64, compare, to_host_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import paged_kv_cache_tables_amd as pkv
+    pkv.load_library()
+    return torch
+
+
+def oracle_after_append(wl):
+    return oracle.kv_append(wl.k_cache, wl.v_cache, wl.k_new, wl.v_new, wl.slot_mapping)
+
+
+def sample_rows(wl, n_decode=None, per_prefill=None, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = []
+    qsl = wl.query_start_loc
+    for s in range(wl.num_seqs):
+        a, b = int(qsl[s]), int(qsl[s + 1])
+        if b - a == 1:
+            rows.append(a)
+        elif b - a > 1:
+            q = b - a
+            pick = {0, 1, q - 1, q // 2}
+            for edge in (31, 32, 63, 64, 127, 128, 255, 256):
+                if edge < q:
+                    pick.add(edge)
+            if per_prefill:
+                pick.update(rng.choice(q, size=min(per_prefill, q), replace=False).tolist())
+            rows.extend(a + j for j in sorted(pick))
+    if n_decode is not None:
+        dec = [r for r in rows if wl.query_lens[np.searchsorted(qsl, r, side="right") - 1] == 1]
+        keep = set(rng.choice(dec, size=min(n_decode, len(dec)), replace=False).tolist()) if dec else set()
+        rows = [r for r in rows if r in keep or r not in set(dec)]
+    return sorted(rows)
+
+
+def run_and_check(wl, rows=None, label=""):
+    db = DeviceBatch(wl)
+    db.step()
+    import torch
+    torch.cuda.synchronize()
+    k2, v2 = oracle_after_append(wl)
+    ref = oracle.paged_attention(wl.q, k2, v2, wl.block_tables, wl.seq_lens, wl.query_start_loc,
+                                 wl.num_kv_heads, wl.scale, rows=rows)
+    out = to_host_bits(db.out)
+    stats = compare(out, ref, rows=rows, label=label or wl.name)
+    return db, out, stats
+
+
+# ---------------------------------------------------------------------------
+# kv_append: bit-exact over the whole pool
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_append_bit_exact_whole_pool(cfg):
+    print(f"append config {cfg}", flush=True)
+    wl = W.make_config(cfg)
+    db = DeviceBatch(wl)
+    db.append()
+    k2, v2 = oracle_after_append(wl)
+    assert np.array_equal(to_host_bits(db.k_cache), k2)
+    assert np.array_equal(to_host_bits(db.v_cache), v2)
+
+
+def test_append_skips_padding_slots():
+    wl = W.config0()
+    wl.slot_mapping = wl.slot_mapping.copy()
+    wl.slot_mapping[[1, 4]] = -1
+    db = DeviceBatch(wl)
+    db.append()
+    k2, v2 = oracle.kv_append(wl.k_cache, wl.v_cache, wl.k_new, wl.v_new, wl.slot_mapping)
+    assert np.array_equal(to_host_bits(db.k_cache), k2)
+    assert np.array_equal(to_host_bits(db.v_cache), v2)
+
+
+# ---------------------------------------------------------------------------
+# attention parity on the five configurations
+# ---------------------------------------------------------------------------
+
+def test_config0_all_rows_and_length_one_exact():
+    wl = W.config0()
+    db, out, stats = run_and_check(wl)
+    # sequence 0 has a single token: the output is its V row, bit for bit
+    G = wl.num_q_heads // wl.num_kv_heads
+    for g in range(wl.num_q_heads):
+        assert np.array_equal(out[0, g], wl.v_new[0, g // G])
+
+
+def test_config0_variant_b():
+    run_and_check(W.config0(variant="B"))
+
+
+def test_config1_llama8b_decode_all_rows():
+    run_and_check(W.config1())
+
+
+def test_config2_70b_decode_sampled_rows():
+    wl = W.config2()
+    run_and_check(wl, rows=sample_rows(wl, n_decode=64))
+
+
+def test_config3_mixed_prefix_sampled_rows():
+    wl = W.config3()
+    run_and_check(wl, rows=sample_rows(wl, per_prefill=24))
+
+
+def test_config4_long_context_all_rows():
+    wl = W.config4()
+    run_and_check(wl)
+
+
+# ---------------------------------------------------------------------------
+# shapes and edge cases
+# ---------------------------------------------------------------------------
+
+EDGE = [
+    # name, seq_specs (L, q), Hq, Hkv, D, bs
+    ("bs8-d128-g4", [(1, 1), (9, 1), (700, 1), (130, 3), (300, 300)], 8, 2, 128, 8),
+    ("bs32-d128-g8", [(33, 1), (1025, 1), (2000, 64), (64, 64)], 16, 2, 128, 32),
+    ("d64-g1-mha", [(5, 1), (513, 1), (100, 37), (1, 1)], 4, 4, 64, 16),
+    ("d64-g16", [(17, 1), (4000, 1), (200, 150)], 16, 1, 64, 16),
+    ("d128-g2", [(2, 2), (3, 1), (65, 65), (1100, 1)], 4, 2, 128, 16),
+    ("mqa-d128-g16", [(777, 1), (300, 130)], 16, 1, 128, 16),
+    ("split-tails", [(511, 1), (512, 1), (513, 1), (1023, 1), (1024, 1), (1025, 1), (64, 1), (65, 1)],
+     8, 2, 128, 16),
+    ("long-single", [(20000, 1)], 32, 8, 128, 16),
+    ("chunk-from-zero", [(512, 512), (97, 97)], 32, 8, 128, 16),
+]
+
+
+@pytest.mark.parametrize("name,specs,Hq,Hkv,D,bs", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_shapes(name, specs, Hq, Hkv, D, bs):
+    wl = W.custom(name, specs, Hq, Hkv, D, bs, seed=len(name))
+    run_and_check(wl)
+
+
+def test_sequences_without_rows_and_interleaved_order():
+    specs = [(40, 1), (25, 0), (300, 20), (9, 0), (1, 1), (200, 1)]
+    wl = W.custom("zero-rows", specs, 8, 2, 128, 16, seed=3, row_order=[3, 0, 5, 2, 1, 4])
+    run_and_check(wl)
+
+
+def test_empty_batch_is_a_no_op(gpu):
+    torch = gpu
+    import paged_kv_cache_tables_amd as pkv
+    k = torch.zeros((4, 16, 2, 64), dtype=torch.bfloat16, device="cuda:0")
+    q = torch.zeros((0, 4, 64), dtype=torch.bfloat16, device="cuda:0")
+    out = torch.zeros_like(q)
+    i32 = dict(dtype=torch.int32, device="cuda:0")
+    pkv.paged_attention(out, q, k, k, torch.zeros((0, 1), **i32), torch.zeros(0, **i32),
+                        torch.zeros(1, **i32), 0.125, 0)
+    pkv.kv_append(torch.zeros((0, 2, 64), dtype=torch.bfloat16, device="cuda:0"),
+                  torch.zeros((0, 2, 64), dtype=torch.bfloat16, device="cuda:0"),
+                  torch.zeros(0, dtype=torch.int64, device="cuda:0"), k, k)
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# invariants on the GPU path
+# ---------------------------------------------------------------------------
+
+def test_poisoned_slots_do_not_change_the_output():
+    outs = []
+    for poison in (W.BF16_QNAN, W.BF16_PINF, W.BF16_NINF, np.uint16(0)):
+        wl = W.config0(poison=poison)
+        db = DeviceBatch(wl)
+        db.step()
+        outs.append(to_host_bits(db.out))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    wl = W.custom("poison-mixed", [(70, 1), (300, 45), (1500, 1)], 8, 2, 128, 16, seed=9,
+                  poison=W.BF16_PINF)
+    wl2 = W.custom("poison-mixed", [(70, 1), (300, 45), (1500, 1)], 8, 2, 128, 16, seed=9,
+                   poison=W.BF16_QNAN)
+    a, b = DeviceBatch(wl), DeviceBatch(wl2)
+    a.step(); b.step()
+    assert np.array_equal(to_host_bits(a.out), to_host_bits(b.out))
+
+
+def test_run_to_run_determinism():
+    wl = W.config3()
+    db = DeviceBatch(wl)
+    db.step()
+    first = to_host_bits(db.out)
+    for _ in range(2):
+        db.attend()
+        assert np.array_equal(to_host_bits(db.out), first)
+
+
+def test_prefix_sharing_equals_private_copies():
+    wl = W.config3()
+    db = DeviceBatch(wl)
+    db.step()
+    shared = to_host_bits(db.out)
+    # give every sharer its own copy of the 64 prefix blocks
+    sharers = wl.meta["sharers"]
+    import torch
+    extra = 64 * (len(sharers) - 1)
+    NB2 = wl.num_blocks + extra
+    k = torch.empty((NB2,) + db.k_cache.shape[1:], dtype=db.k_cache.dtype, device=db.k_cache.device)
+    v = torch.empty_like(k)
+    k[:wl.num_blocks] = db.k_cache
+    v[:wl.num_blocks] = db.v_cache
+    bt = wl.block_tables.copy()
+    nxt = wl.num_blocks
+    prefix = torch.from_numpy(bt[sharers[0], :64].astype(np.int64)).cuda()
+    for s in sharers[1:]:
+        ids = np.arange(nxt, nxt + 64)
+        nxt += 64
+        k[nxt - 64:nxt] = db.k_cache[prefix]
+        v[nxt - 64:nxt] = db.v_cache[prefix]
+        bt[s, :64] = ids
+    db.k_cache, db.v_cache = k, v
+    db.bt = torch.from_numpy(bt.astype(np.int32)).cuda()
+    db.attend()
+    assert np.array_equal(to_host_bits(db.out), shared)
+
+
+def test_caller_workspace_and_stream(gpu):
+    torch = gpu
+    import paged_kv_cache_tables_amd as pkv
+    wl = W.config1(num_seqs=8)
+    db = DeviceBatch(wl)
+    db.append()
+    need = pkv.workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                               wl.max_blocks_per_seq, wl.block_size)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        db.attend(workspace=ws)
+    s.synchronize()
+    got = to_host_bits(db.out)
+    db.out.zero_()
+    db.attend()
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_bits(db.out), got)
+    with pytest.raises(pkv.PagedKVError):
+        db.attend(workspace=ws[: need - 256])
