@@ -99,7 +99,8 @@ PKV_API int64_t kv_bytes_per_token(int64_t num_layers, int64_t num_kv_heads, int
  *
  *   k_new, v_new   device, bf16 [num_tokens, num_kv_heads, head_dim], read only.
  *   slot_mapping   device, int64 [num_tokens].
- *   num_tokens     >= 0; 0 enqueues nothing and returns PKV_OK.
+ *   num_tokens     >= 0; 0 enqueues nothing and returns PKV_OK (pointers may
+ *                  then be NULL).
  *   k_cache, v_cache  device, bf16 pools (see conventions), written in place.
  *   num_blocks, block_size, num_kv_heads, head_dim   pool shape; > 0.
  *   head_dim       a multiple of 8 (16-byte rows chunks); 64 and 128 are tuned.

@@ -67,13 +67,13 @@ int kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
               int32_t num_kv_heads, int32_t head_dim, void* stream) {
   if (num_tokens < 0 || num_blocks <= 0 || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0)
     return PKV_EINVAL;
-  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PKV_EINVAL;
   if (head_dim % 8 != 0) return PKV_EUNSUPPORTED;   // rows move in 16-byte chunks
+  if (num_blocks > INT64_MAX / block_size) return PKV_EINVAL;
+  if (num_tokens == 0) return PKV_OK;               // empty inputs may carry null pointers
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PKV_EINVAL;
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(slot_mapping, 8))
     return PKV_EINVAL;
-  if (num_blocks > INT64_MAX / block_size) return PKV_EINVAL;
-  if (num_tokens == 0) return PKV_OK;
   const int row_chunks = num_kv_heads * head_dim / 8;
   hipError_t e = pkv::launch_append(k_new, v_new, slot_mapping, num_tokens, k_cache, v_cache,
                                     num_blocks * block_size, row_chunks, (hipStream_t)stream);

@@ -71,6 +71,7 @@ def append_args(**over):
     (dict(head_dim=60), PKV_EUNSUPPORTED),
     (dict(k_cache=FAKE + 8), PKV_EINVAL),          # not 16-byte aligned
     (dict(num_tokens=0), PKV_OK),                   # nothing to do, nothing launched
+    (dict(num_tokens=0, k_new=None, slot_mapping=None), PKV_OK),   # empty tensors have null data
 ])
 def test_kv_append_validation(lib, over, expect):
     assert lib.kv_append(*append_args(**over)) == expect
