@@ -31,20 +31,38 @@ namespace pkv {
 
 namespace {
 
-constexpr int kTile = 64;     // tokens per wave iteration (one per lane)
-constexpr int kWaves = 4;
+constexpr int kTile = 64;     // tokens per wave iteration (one per lane in the QK step)
+constexpr int kWaves = 4;     // waves per workgroup; each walks its own tiles of the split
+constexpr int kVPL = 4;       // V elements per lane per load (8-byte loads)
+
+// 16-byte / 8-byte vector types for the V loads.
+template <int N> struct VecOf;
+template <> struct VecOf<8> { typedef uint4 T; };
+template <> struct VecOf<4> { typedef uint2 T; };
+
+__device__ __forceinline__ void unpack(const uint4& v, float* f) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+__device__ __forceinline__ void unpack(const uint2& v, float* f) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+}
 
 template <int D, int G, int BS>
-__global__ __launch_bounds__(256, 2) void decode_split_kernel(AttnParams p) {
-  constexpr int CH = D / 8;            // 16-byte chunks per K row
-  constexpr int RPI = kWave / CH;      // K rows staged per wave-wide load
-  constexpr int NSTAGE = kTile / RPI;  // loads per lane per tile
-  constexpr int LPT = D / 2;           // lanes per V row (4 bytes each)
-  constexpr int TPS = kWave / LPT;     // V rows per wave-wide load
-  static_assert(BS % RPI == 0 && BS % TPS == 0, "rows of one load must share a block");
+__global__ __launch_bounds__(kWaves * kWave) void decode_split_kernel(AttnParams p) {
+  constexpr int CH = D / 8;              // 16-byte chunks per K row
+  constexpr int VPL = kVPL;
+  constexpr int LPR = D / VPL;           // lanes per V row
+  constexpr int TPI = kWave / LPR;       // V rows per wave-wide load
+  constexpr int NV = kTile / TPI;        // V loads per lane per tile
+  constexpr int NBT = kTile / BS;        // blocks spanned by one tile
+  typedef typename VecOf<VPL>::T VT;
+  static_assert(BS % TPI == 0 && kTile % BS == 0, "rows of one V load must share a block");
 
-  __shared__ uint4 ktile[kWaves][kTile][CH];
-  __shared__ float ptile[kWaves][kTile][G];
+  constexpr int GP = G < 4 ? 4 : G;      // heads padded to a float4
+  __shared__ float4 ptile[kWaves][kTile][GP / 4];   // softmax weights of the current tile
+  __shared__ float sm_o[kWaves][G][D];
+  __shared__ float sm_ml[kWaves][G][2];
 
   const int split = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int row0 = p.qsl[s];
@@ -66,46 +84,75 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(AttnParams p) {
   const uint16_t* vbase = p.v_cache + (size_t)h * D;
   const uint4* qv = reinterpret_cast<const uint4*>(p.q + ((size_t)row0 * Hq + (size_t)h * G) * D);
   const float c = p.scale_log2;
+  const int vt = lane / LPR;                     // V token group of this lane
+  const int vd = (lane % LPR) * VPL;             // first V dim of this lane
+  const int nblocks = (unsigned)p.num_blocks > 0x7fffffffu ? 0x7fffffff : (int)p.num_blocks;
 
-  float m_run[G], l_part[G], o0[G], o1[G];
+  float m_run[G], l_part[G], o[G][VPL];
 #pragma unroll
-  for (int g = 0; g < G; ++g) { m_run[g] = -INFINITY; l_part[g] = 0.f; o0[g] = 0.f; o1[g] = 0.f; }
+  for (int g = 0; g < G; ++g) {
+    m_run[g] = -INFINITY; l_part[g] = 0.f;
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) o[g][j] = 0.f;
+  }
 
-  for (int ts = t_begin + w * kTile; ts < t_end; ts += kWaves * kTile) {
+  const size_t blk_bytes = (size_t)BS * row_stride * 2;
+  const uint32_t row_bytes = (uint32_t)(row_stride * 2);
+  const int ntiles = (t_end - t_begin + kTile - 1) / kTile;     // tiles of the split
+  for (int tile = w; tile < ntiles; tile += kWaves) {
+    const int ts = t_begin + tile * kTile;
     const int nvalid = min(kTile, t_end - ts);
 
-    // ---- stage the K tile: row r, chunk cc -> LDS [r][cc ^ (r % CH)] ----
+    // Block-table entries of the tile (wave-uniform scalar loads).  Entries past the end,
+    // or outside the pool, become block 0: a safe address whose rows the masks ignore.
+    int bts[NBT];
 #pragma unroll
-    for (int it = 0; it < NSTAGE; ++it) {
-      const int r = it * RPI + lane / CH;
-      const int cc = lane % CH;
-      const int first = ts + it * RPI;           // wave-uniform
-      uint4 val = make_uint4(0u, 0u, 0u, 0u);
-      if (first < t_end) {
-        const int blk = bt_row[uniform(first / BS)];
-        const int tok = ts + r;
-        if (tok < t_end && (unsigned)blk < (unsigned)p.num_blocks)
-          val = *reinterpret_cast<const uint4*>(kbase + ((size_t)blk * BS + tok % BS) * row_stride + cc * 8);
-      }
-      ktile[w][r][cc ^ (r % CH)] = val;
+    for (int j = 0; j < NBT; ++j) {
+      const int b = (j * BS < nvalid) ? bt_row[uniform((ts + j * BS) / BS)] : 0;
+      bts[j] = (unsigned)b < (unsigned)nblocks ? b : 0;
     }
-    wave_lds_sync();
 
-    // ---- QK: lane owns token `lane` ----
+    // ---- issue all loads of the tile: K (lane = token, whole row), V (lane = VPL dims) ----
+    uint4 kreg[CH];
+    {
+      int blk = bts[0];
+#pragma unroll
+      for (int j = 1; j < NBT; ++j) if (lane / BS == j) blk = bts[j];
+      const uint4* src = reinterpret_cast<const uint4*>(
+          reinterpret_cast<const char*>(kbase) + (size_t)blk * blk_bytes + (uint32_t)(lane % BS) * row_bytes);
+#pragma unroll
+      for (int cc = 0; cc < CH; ++cc) kreg[cc] = src[cc];
+    }
+    VT vreg[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const char* base = reinterpret_cast<const char*>(vbase) + (size_t)bts[(TPI * i) / BS] * blk_bytes;
+      const uint32_t off = (uint32_t)((TPI * i) % BS + vt) * row_bytes + (uint32_t)vd * 2;
+      vreg[i] = *reinterpret_cast<const VT*>(base + off);
+    }
+
+    // ---- QK: lane owns token ts + lane; q sits in scalar registers ----
     float acc[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) acc[g] = 0.f;
+    // q is re-read from the scalar cache every tile: an opaque zero offset stops the
+    // compiler from hoisting G*D/2 values out of the loop into vector registers.
+    int zero;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
+    // constant address space: uniform loads from it are always scalar (s_load)
+    typedef const __attribute__((address_space(4))) uint32_t cu32;
+    cu32* qt = (cu32*)(qv + zero);
 #pragma unroll
     for (int cc = 0; cc < CH; ++cc) {
-      const uint4 kk = ktile[w][lane][cc ^ (lane % CH)];
+      const uint4 kk = kreg[cc];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        const uint4 qq = qv[g * CH + cc];
+        cu32* qq = qt + 4 * (g * CH + cc);
         float a = acc[g];
-        a = dot2_bf16(qq.x, kk.x, a);
-        a = dot2_bf16(qq.y, kk.y, a);
-        a = dot2_bf16(qq.z, kk.z, a);
-        a = dot2_bf16(qq.w, kk.w, a);
+        a = dot2_bf16(qq[0], kk.x, a);
+        a = dot2_bf16(qq[1], kk.y, a);
+        a = dot2_bf16(qq[2], kk.z, a);
+        a = dot2_bf16(qq[3], kk.w, a);
         acc[g] = a;
       }
     }
@@ -113,82 +160,86 @@ __global__ __launch_bounds__(256, 2) void decode_split_kernel(AttnParams p) {
     // ---- online softmax (exp2 domain) ----
     const bool valid = lane < nvalid;
     float alpha[G];
+    float pe[GP];
+#pragma unroll
+    for (int g = G; g < GP; ++g) pe[g] = 0.f;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float sc = valid ? acc[g] * c : -INFINITY;
       const float mn = fmaxf(m_run[g], wave_max(sc));   // finite: lane 0 is always valid
       alpha[g] = exp2f(m_run[g] - mn);                  // 0 on the first tile
-      const float pe = valid ? exp2f(sc - mn) : 0.f;
-      l_part[g] = l_part[g] * alpha[g] + pe;
+      pe[g] = valid ? exp2f(sc - mn) : 0.f;
+      l_part[g] = l_part[g] * alpha[g] + pe[g];
       m_run[g] = mn;
-      ptile[w][lane][g] = pe;
     }
+#pragma unroll
+    for (int g4 = 0; g4 < GP / 4; ++g4)
+      ptile[w][lane][g4] = make_float4(pe[4 * g4], pe[4 * g4 + 1], pe[4 * g4 + 2], pe[4 * g4 + 3]);
     wave_lds_sync();
 
-    // ---- PV: lane owns dims 2*(lane % LPT) and +1 ----
+    // ---- PV: lane owns VPL dims of every TPI-th token ----
 #pragma unroll
-    for (int g = 0; g < G; ++g) { o0[g] *= alpha[g]; o1[g] *= alpha[g]; }
-    const int dpair = lane % LPT;
-    for (int rr = 0; rr < nvalid; rr += TPS) {
-      const int r = rr + lane / LPT;
-      const int blk = bt_row[uniform((ts + rr) / BS)];
-      float v0 = 0.f, v1 = 0.f;
-      if (r < nvalid && (unsigned)blk < (unsigned)p.num_blocks) {
-        const int tok = ts + r;
-        const uint32_t vw = *reinterpret_cast<const uint32_t*>(
-            vbase + ((size_t)blk * BS + tok % BS) * row_stride + 2 * dpair);
-        v0 = bf16_lo(vw);
-        v1 = bf16_hi(vw);
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) o[g][j] *= alpha[g];
+    const int vlim = nvalid - vt;                       // token slot i is valid iff TPI*i < vlim
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      // keep the weight reads next to their use (hoisting all of them costs registers)
+      if (i % 4 == 0) __builtin_amdgcn_sched_barrier(0);
+      const int r = TPI * i + vt;
+      float vf[VPL];
+      unpack(vreg[i], vf);
+      if (TPI * i < vlim) {} else {                     // rows past the end may hold NaN; weight is 0
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) vf[j] = 0.f;
+      }
+      float pw[GP];
+#pragma unroll
+      for (int g4 = 0; g4 < GP / 4; ++g4) {
+        const float4 t4 = ptile[w][r][g4];
+        pw[4 * g4] = t4.x; pw[4 * g4 + 1] = t4.y; pw[4 * g4 + 2] = t4.z; pw[4 * g4 + 3] = t4.w;
       }
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        const float pw = ptile[w][r][g];
-        o0[g] = fmaf(pw, v0, o0[g]);
-        o1[g] = fmaf(pw, v1, o1[g]);
-      }
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) o[g][j] = fmaf(pw[g], vf[j], o[g][j]);
     }
     wave_lds_sync();
   }
 
-  // ---- combine the 4 waves ----
+  // ---- combine: token groups inside the wave, then the waves ----
   float l_tot[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     l_tot[g] = wave_sum(l_part[g]);
-    if (TPS > 1) {  // lanes of different token groups hold partial sums of the same dims
-      o0[g] += __shfl_xor(o0[g], LPT, kWave);
-      o1[g] += __shfl_xor(o1[g], LPT, kWave);
-    }
-  }
-  __syncthreads();                                   // every wave is done with its K tiles
-  float* sm_o = reinterpret_cast<float*>(&ktile[0][0][0]);   // [kWaves][G][D]
-  float* sm_ml = sm_o + kWaves * G * D;                       // [kWaves][G][2]
-  if (lane < LPT) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      sm_o[(w * G + g) * D + 2 * lane] = o0[g];
-      sm_o[(w * G + g) * D + 2 * lane + 1] = o1[g];
-    }
+    for (int msk = LPR; msk < kWave; msk *= 2)
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) o[g][j] += __shfl_xor(o[g][j], msk, kWave);
+  }
+  if (lane < LPR) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int j = 0; j < VPL; ++j) sm_o[w][g][vd + j] = o[g][j];
   }
   if (lane == 0) {
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      sm_ml[(w * G + g) * 2] = m_run[g];
-      sm_ml[(w * G + g) * 2 + 1] = l_tot[g];
-    }
+    for (int g = 0; g < G; ++g) { sm_ml[w][g][0] = m_run[g]; sm_ml[w][g][1] = l_tot[g]; }
   }
   __syncthreads();
   for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
     const int g = e / D, d = e % D;
     float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm_ml[(ww * G + g) * 2]);
+    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm_ml[ww][g][0]);
     float O = 0.f, Ls = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
-      const float f = exp2f(sm_ml[(ww * G + g) * 2] - M);   // 0 for a wave without tokens
-      Ls = fmaf(f, sm_ml[(ww * G + g) * 2 + 1], Ls);
-      O = fmaf(f, sm_o[(ww * G + g) * D + d], O);
+      const float f = exp2f(sm_ml[ww][g][0] - M);   // 0 for a wave without tokens
+      Ls = fmaf(f, sm_ml[ww][g][1], Ls);
+      O = fmaf(f, sm_o[ww][g][d], O);
     }
     const int qh = h * G + g;
     if (nsplit == 1) {
