@@ -114,6 +114,9 @@ def main():
     ap.add_argument("--copies", type=int, default=3, help="device copies of the batch cycled per step")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the step, run a plain device copy of MIB MiB --steps times "
+                         "(reference kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -130,6 +133,17 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs the GPU"
     dev = torch.device("cuda:0")
     pkv.load_library()
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        x = torch.ones(n, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        for _ in range(args.steps):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
+                          "steps": args.steps}), flush=True)
+        return
 
     log(f"generating config {args.config} ...")
     wl = workloads.make_config(args.config)

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace pkv {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -32,6 +34,21 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          c, false);
 }
 
+// 2^x with the hardware instruction (results below 2^-126 flush to zero, which for
+// softmax weights relative to a maximum weight of 1 is far below fp32 resolution).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Compile-time integers and an unrolled loop over them (indices stay constants, so
+// register arrays indexed by them stay in registers).
+template <int V> using IntC = std::integral_constant<int, V>;
+template <int N, typename F, int I = 0>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(IntC<I>());
+    static_for<N, F, I + 1>(static_cast<F&&>(f));
+  }
+}
+
 // Wave-uniform copy of a value (lands in a scalar register).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
@@ -42,16 +59,45 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-  return v;
+// Cross-lane reductions over a whole 64-lane wave built from DPP row operations
+// (quad swaps, half-row and row mirrors inside each 16-lane row, then row
+// broadcasts 15 and 31 towards lane 63), finished by one readlane: the result
+// is wave-uniform.  No LDS traffic.
+template <typename Op>
+__device__ __forceinline__ float wave_reduce_dpp(float v, Op op) {
+  auto dpp = [](float x, int ctrl_sel) -> float {
+    int xi = __float_as_int(x);
+    int r;
+    switch (ctrl_sel) {
+      case 0: r = __builtin_amdgcn_update_dpp(xi, xi, 0xB1, 0xF, 0xF, false); break;   // quad_perm [1,0,3,2]
+      case 1: r = __builtin_amdgcn_update_dpp(xi, xi, 0x4E, 0xF, 0xF, false); break;   // quad_perm [2,3,0,1]
+      case 2: r = __builtin_amdgcn_update_dpp(xi, xi, 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+      case 3: r = __builtin_amdgcn_update_dpp(xi, xi, 0x140, 0xF, 0xF, false); break;  // row_mirror
+      case 4: r = __builtin_amdgcn_update_dpp(xi, xi, 0x142, 0xA, 0xF, false); break;  // row_bcast:15 -> rows 1,3
+      default: r = __builtin_amdgcn_update_dpp(xi, xi, 0x143, 0xC, 0xF, false); break; // row_bcast:31 -> rows 2,3
+    }
+    return __int_as_float(r);
+  };
+  v = op(v, dpp(v, 0));
+  v = op(v, dpp(v, 1));
+  v = op(v, dpp(v, 2));
+  v = op(v, dpp(v, 3));   // every lane holds its row's result
+  v = op(v, dpp(v, 4));   // lanes of rows 1 and 3 also cover rows 0 and 2
+  v = op(v, dpp(v, 5));   // lane 63 covers the wave
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
+struct MaxOp { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+struct SumOp { __device__ float operator()(float a, float b) const { return a + b; } };
+
+__device__ __forceinline__ float wave_max(float v) { return wave_reduce_dpp(v, MaxOp()); }
+__device__ __forceinline__ float wave_sum(float v) { return wave_reduce_dpp(v, SumOp()); }
+
+// v[lane % 32] + v[32 + lane % 32] in every lane (the two half-waves added).
+__device__ __forceinline__ float half_wave_sum(float v) {
+  const int x = __float_as_int(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
 }
 
 }  // namespace pkv

@@ -9,21 +9,29 @@
 // what the merge kernel does across splits.  Keys and values are reached
 // through the sequence's block table ("Under the Hood: PagedAttention").
 //
-// Work decomposition (gfx950, 64-lane waves):
-//   grid  = (split, kv head, sequence); block = 4 waves.
-//   Every wave walks its own 64-token tiles of the split (tiles w, w+4, ...):
-//     * the K tile is staged through LDS with coalesced 16-byte loads (16
-//       lanes per 256-byte row) and read back one row per lane (XOR-swizzled
-//       16-byte chunks, conflict-free), so lane t owns token t;
-//     * QK: lane t forms the G dot products of its key with the G query heads
-//       of the GQA group (packed bf16 dot2 with fp32 accumulation) -- all G
-//       heads share the one K read, and no cross-lane reduction is needed;
-//     * softmax: per head, a wave max (shuffles), exp2, per-lane partial sums;
-//       probabilities go to LDS;
-//     * PV: lane d owns two output dims of all G heads; each V row is one
-//       coalesced 256-byte load (4 bytes per lane), weights are LDS broadcasts.
-//   The 4 waves' (O, m, l) are combined through LDS; a sequence with one split
-//   writes bf16 output directly, otherwise fp32 partials go to the workspace.
+// Why matrix cores for a bandwidth-bound step: with a GQA group of G query
+// heads sharing each K/V row, decode performs G floating-point operations per
+// byte of K/V (G*D multiply-adds for QK and again for PV per 4*D bytes).  At
+// 8 TB/s and G = 8 that is 64 TFLOP/s of fp32 FMAs -- 81% of the chip's
+// non-packed fp32 vector peak before any softmax work -- so vector-ALU decode
+// would be ALU-bound below the HBM roofline.  The group's products are real
+// dense contractions ([G x D] x [D x T]), so they run on bf16 MFMA with fp32
+// accumulation and the vector ALUs are left with the softmax.
+//
+// Layout (gfx950, one 64-lane wave per workgroup, v_mfma_f32_16x16x32_bf16):
+//   grid = (split, kv head, sequence); the wave walks the split's 64-token tiles.
+//   * Scores transposed, S^T = K Q^T: A = K rows (16 tokens x 32 dims per
+//     MFMA: each lane loads 16 contiguous bytes of one row straight from the
+//     pool), B = the G query rows (heads padded to 16 columns, loaded once).
+//     Each lane's accumulator column is one head, so the per-head max and sum
+//     over the tile need a local reduction plus two lane exchanges.
+//   * Output transposed, O^T = V^T P^T: B = P^T is the score accumulator
+//     converted to bf16 in place; A = V^T comes from an LDS copy of the V
+//     tile stored transposed ([dim][token], bf16 pairs along tokens).
+//   * The next tile's K loads go out as soon as this tile's QK products have
+//     consumed the K registers; V loads are issued with K at the tile start.
+//   A sequence with one split writes bf16 output directly, otherwise fp32
+//   partials (O, m, l) go to the workspace for the merge kernel.
 #include "common.h"
 #include "kernels.h"
 
@@ -31,223 +39,239 @@ namespace pkv {
 
 namespace {
 
-constexpr int kTile = 64;     // tokens per wave iteration (one per lane in the QK step)
-constexpr int kWaves = 4;     // waves per workgroup; each walks its own tiles of the split
-constexpr int kVPL = 4;       // V elements per lane per load (8-byte loads)
-
-// 16-byte / 8-byte vector types for the V loads.
-template <int N> struct VecOf;
-template <> struct VecOf<8> { typedef uint4 T; };
-template <> struct VecOf<4> { typedef uint2 T; };
-
-__device__ __forceinline__ void unpack(const uint4& v, float* f) {
-  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
-  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
-}
-__device__ __forceinline__ void unpack(const uint2& v, float* f) {
-  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
-}
+constexpr int kTile = 64;        // tokens per tile
+constexpr int kVT = kTile + 4;   // padded row (in tokens) of the transposed V tile
 
 template <int D, int G, int BS>
-__global__ __launch_bounds__(kWaves * kWave) void decode_split_kernel(AttnParams p) {
-  constexpr int CH = D / 8;              // 16-byte chunks per K row
-  constexpr int VPL = kVPL;
-  constexpr int LPR = D / VPL;           // lanes per V row
-  constexpr int TPI = kWave / LPR;       // V rows per wave-wide load
-  constexpr int NV = kTile / TPI;        // V loads per lane per tile
-  constexpr int NBT = kTile / BS;        // blocks spanned by one tile
-  typedef typename VecOf<VPL>::T VT;
-  static_assert(BS % TPI == 0 && kTile % BS == 0, "rows of one V load must share a block");
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void decode_split_kernel(AttnParams p) {
+  constexpr int CH = D / 8;              // 16-byte chunks per row
+  constexpr int KS = D / 32;             // k-steps of QK (32 dims each)
+  constexpr int DB = D / 16;             // 16-dim blocks of the output
+  constexpr int TB = kTile / 16;         // 16-token blocks of a tile
+  constexpr int NBT = kTile / BS;        // pool blocks spanned by a tile
+  constexpr int NVI = (kTile / 2) * CH / kWave;   // (token pair, chunk) items per lane
+  static_assert(G <= 16, "a GQA group is one 16-column MFMA tile");
+  static_assert(kTile % BS == 0, "tiles start on block boundaries");
 
-  constexpr int GP = G < 4 ? 4 : G;      // heads padded to a float4
-  __shared__ float4 ptile[kWaves][kTile][GP / 4];   // softmax weights of the current tile
-  __shared__ float sm_o[kWaves][G][D];
-  __shared__ float sm_ml[kWaves][G][2];
+  __shared__ __attribute__((aligned(16))) uint32_t vt_tile[D][kVT / 2];
 
   const int split = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
   const int row0 = p.qsl[s];
   if (p.qsl[s + 1] - row0 != 1) return;          // not a decode row
   if (row0 < 0 || row0 >= p.num_q_tokens) return;
-  // lengths beyond what the table row can map are clamped (caller error)
-  const int L = min(p.seq_lens[s], p.max_blocks * BS);
+  const int L = min(p.seq_lens[s], p.max_blocks * BS);   // clamp a length the table cannot map
   const int t_begin = split * p.split_tokens;
   if (t_begin >= L) return;                      // split past the end of the sequence
   const int t_end = min(t_begin + p.split_tokens, L);
   const int nsplit = (L + p.split_tokens - 1) / p.split_tokens;
 
-  const int lane = threadIdx.x & (kWave - 1);
-  const int w = uniform(threadIdx.x / kWave);
+  const int lane = threadIdx.x;
+  const int n = lane & 15;                       // accumulator column: query head of the group
+  const int kg = lane >> 4;                      // k-group / accumulator row group
   const int Hq = p.Hkv * G;
   const int* bt_row = p.block_tables + (size_t)s * p.max_blocks;
   const size_t row_stride = (size_t)p.Hkv * D;   // elements per pool slot
-  const uint16_t* kbase = p.k_cache + (size_t)h * D;
-  const uint16_t* vbase = p.v_cache + (size_t)h * D;
-  const uint4* qv = reinterpret_cast<const uint4*>(p.q + ((size_t)row0 * Hq + (size_t)h * G) * D);
-  const float c = p.scale_log2;
-  const int vt = lane / LPR;                     // V token group of this lane
-  const int vd = (lane % LPR) * VPL;             // first V dim of this lane
-  const int nblocks = (unsigned)p.num_blocks > 0x7fffffffu ? 0x7fffffff : (int)p.num_blocks;
-
-  float m_run[G], l_part[G], o[G][VPL];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m_run[g] = -INFINITY; l_part[g] = 0.f;
-#pragma unroll
-    for (int j = 0; j < VPL; ++j) o[g][j] = 0.f;
-  }
-
+  const char* kbase = reinterpret_cast<const char*>(p.k_cache + (size_t)h * D);
+  const char* vbase = reinterpret_cast<const char*>(p.v_cache + (size_t)h * D);
+  const int nblocks = p.num_blocks > 0x7fffffff ? 0x7fffffff : (int)p.num_blocks;
   const size_t blk_bytes = (size_t)BS * row_stride * 2;
   const uint32_t row_bytes = (uint32_t)(row_stride * 2);
-  const int ntiles = (t_end - t_begin + kTile - 1) / kTile;     // tiles of the split
-  for (int tile = w; tile < ntiles; tile += kWaves) {
-    const int ts = t_begin + tile * kTile;
-    const int nvalid = min(kTile, t_end - ts);
+  const float c = p.scale_log2;
 
-    // Block-table entries of the tile (wave-uniform scalar loads).  Entries past the end,
-    // or outside the pool, become block 0: a safe address whose rows the masks ignore.
-    int bts[NBT];
+  // ---- Q^T as the B operand: head n, dims ks*32 + kg*8 .. +8 (zero for padding heads) ----
+  bf16x8 qreg[KS];
+  {
+    const uint16_t* qp = p.q + ((size_t)row0 * Hq + (size_t)h * G + (n < G ? n : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (n < G) v = *reinterpret_cast<const uint4*>(qp + ks * 32 + kg * 8);
+      qreg[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  floatx4 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.f;
+
+  // Block-table entries of a tile (wave-uniform scalar loads).  Entries past the end,
+  // or outside the pool, become block 0: a safe address whose rows the masks ignore.
+  auto load_bts = [&](int t0, int* dst) {
 #pragma unroll
     for (int j = 0; j < NBT; ++j) {
-      const int b = (j * BS < nvalid) ? bt_row[uniform((ts + j * BS) / BS)] : 0;
-      bts[j] = (unsigned)b < (unsigned)nblocks ? b : 0;
+      const int b = (t0 + j * BS < t_end) ? bt_row[uniform((t0 + j * BS) / BS)] : 0;
+      dst[j] = (unsigned)b < (unsigned)nblocks ? b : 0;
     }
-
-    // ---- issue all loads of the tile: K (lane = token, whole row), V (lane = VPL dims) ----
-    uint4 kreg[CH];
-    {
-      int blk = bts[0];
+  };
+  // Address of tile row r0 + rl, where r0 (a compile-time multiple of GROUP) is shared by
+  // the wave and rl < GROUP varies per lane.  When a group of GROUP rows lies inside one
+  // pool block, the block base is wave-uniform (scalar) and the lane adds a 32-bit offset;
+  // otherwise the lane picks its block from the tile's table entries.
+  auto row_addr = [&](const char* base, const int* bb, auto r0c, auto groupc, int rl) -> const char* {
+    constexpr int r0 = decltype(r0c)::value, GROUP = decltype(groupc)::value;
+    if constexpr (GROUP <= BS) {
+      const char* b = base + (size_t)bb[r0 / BS] * blk_bytes + (uint32_t)(r0 % BS) * row_bytes;
+      return b + (uint32_t)rl * row_bytes;
+    } else {
+      int blk = bb[r0 / BS];
 #pragma unroll
-      for (int j = 1; j < NBT; ++j) if (lane / BS == j) blk = bts[j];
+      for (int j = 1; j < GROUP / BS; ++j) if (rl / BS == j) blk = bb[r0 / BS + j];
+      return base + (size_t)blk * blk_bytes + (uint32_t)(rl % BS) * row_bytes;
+    }
+  };
+  // K as the A operand: token block tb, lane's row tb*16 + n, dims ks*32 + kg*8.
+  uint4 kreg[TB][KS];
+  auto issue_k = [&](const int* bb) {
+    static_for<TB>([&](auto tbc) {
+      constexpr int tb = decltype(tbc)::value;
       const uint4* src = reinterpret_cast<const uint4*>(
-          reinterpret_cast<const char*>(kbase) + (size_t)blk * blk_bytes + (uint32_t)(lane % BS) * row_bytes);
+          row_addr(kbase, bb, IntC<tb * 16>(), IntC<16>(), n) + kg * 16);
 #pragma unroll
-      for (int cc = 0; cc < CH; ++cc) kreg[cc] = src[cc];
-    }
-    VT vreg[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const char* base = reinterpret_cast<const char*>(vbase) + (size_t)bts[(TPI * i) / BS] * blk_bytes;
-      const uint32_t off = (uint32_t)((TPI * i) % BS + vt) * row_bytes + (uint32_t)vd * 2;
-      vreg[i] = *reinterpret_cast<const VT*>(base + off);
-    }
+      for (int ks = 0; ks < KS; ++ks) kreg[tb][ks] = src[ks * 4];
+    });
+  };
 
-    // ---- QK: lane owns token ts + lane; q sits in scalar registers ----
-    float acc[G];
+  const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
+  int bts[NBT];
+  load_bts(t_begin, bts);
+  issue_k(bts);
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int ts = t_begin + tile * kTile;
+    const int nvalid = min(kTile, t_end - ts);
+    const bool has_next = tile + 1 < ntiles;
+
+    // ---- V tile: item it = (token pair tp, chunk cc), 16 lanes per 256-byte row ----
+    // item it = lane + 64 j = (token pair tp, chunk cc); rows of one j form a group of TPJ
+    constexpr int TPJ = 2 * kWave / CH;          // tokens covered by one j
+    const int vrow = 2 * (lane / CH);            // lane's first row inside the group
+    const int vcc = lane % CH;
+    uint4 va[NVI], vb[NVI];
+    static_for<NVI>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const char* a = row_addr(vbase, bts, IntC<TPJ * j>(), IntC<TPJ>(), vrow) + vcc * 16;
+      va[j] = *reinterpret_cast<const uint4*>(a);
+      vb[j] = *reinterpret_cast<const uint4*>(a + row_bytes);   // row vrow + 1: same block (BS even)
+    });
+    int bts_next[NBT];
 #pragma unroll
-    for (int g = 0; g < G; ++g) acc[g] = 0.f;
-    // q is re-read from the scalar cache every tile: an opaque zero offset stops the
-    // compiler from hoisting G*D/2 values out of the loop into vector registers.
-    int zero;
-    asm volatile("s_mov_b32 %0, 0" : "=s"(zero));
-    // constant address space: uniform loads from it are always scalar (s_load)
-    typedef const __attribute__((address_space(4))) uint32_t cu32;
-    cu32* qt = (cu32*)(qv + zero);
+    for (int j = 0; j < NBT; ++j) bts_next[j] = 0;
+    if (has_next) load_bts(ts + kTile, bts_next);
+
+    // ---- S^T = K Q^T ----
+    floatx4 sacc[TB];
 #pragma unroll
-    for (int cc = 0; cc < CH; ++cc) {
-      const uint4 kk = kreg[cc];
+    for (int tb = 0; tb < TB; ++tb) {
+      sacc[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        cu32* qq = qt + 4 * (g * CH + cc);
-        float a = acc[g];
-        a = dot2_bf16(qq[0], kk.x, a);
-        a = dot2_bf16(qq[1], kk.y, a);
-        a = dot2_bf16(qq[2], kk.z, a);
-        a = dot2_bf16(qq[3], kk.w, a);
-        acc[g] = a;
+      for (int ks = 0; ks < KS; ++ks)
+        sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[tb][ks]), qreg[ks],
+                                                          sacc[tb], 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);           // the next K loads reuse the K registers
+    if (has_next) issue_k(bts_next);
+
+    // ---- online softmax for head n over this tile's tokens (exp2 domain) ----
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = tb * 16 + 4 * kg + i;      // token of this accumulator element
+        const float v = (r < nvalid) ? sacc[tb][i] * c : -INFINITY;
+        sacc[tb][i] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+    const float mn = fmaxf(m_run, tmax);         // finite: token 0 of the tile is valid
+    const float alpha = fast_exp2(m_run - mn);   // 0 on the first tile
+    m_run = mn;
+    float psum = 0.f;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = fast_exp2(sacc[tb][i] - mn);   // 0 for masked tokens
+        sacc[tb][i] = e;
+        psum += e;
+      }
+    l_part = l_part * alpha + psum;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oacc[db][i] *= alpha;
+
+    // ---- V^T into LDS: dword (tp, dim) = bf16 pair (token 2tp, token 2tp+1) ----
+    if (nvalid < kTile) {                        // rows past the end may hold any bits (NaN)
+#pragma unroll
+      for (int j = 0; j < NVI; ++j) {
+        const int tp = (lane + kWave * j) / CH;
+        if (2 * tp >= nvalid) va[j] = make_uint4(0u, 0u, 0u, 0u);
+        if (2 * tp + 1 >= nvalid) vb[j] = make_uint4(0u, 0u, 0u, 0u);
       }
     }
-
-    // ---- online softmax (exp2 domain) ----
-    const bool valid = lane < nvalid;
-    float alpha[G];
-    float pe[GP];
 #pragma unroll
-    for (int g = G; g < GP; ++g) pe[g] = 0.f;
+    for (int j = 0; j < NVI; ++j) {
+      const int it = lane + kWave * j;
+      const int tp = it / CH, cc = it % CH;
+      const uint32_t aw[4] = {va[j].x, va[j].y, va[j].z, va[j].w};
+      const uint32_t bw[4] = {vb[j].x, vb[j].y, vb[j].z, vb[j].w};
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const float sc = valid ? acc[g] * c : -INFINITY;
-      const float mn = fmaxf(m_run[g], wave_max(sc));   // finite: lane 0 is always valid
-      alpha[g] = exp2f(m_run[g] - mn);                  // 0 on the first tile
-      pe[g] = valid ? exp2f(sc - mn) : 0.f;
-      l_part[g] = l_part[g] * alpha[g] + pe[g];
-      m_run[g] = mn;
+      for (int x = 0; x < 4; ++x) {
+        const int d = cc * 8 + 2 * x;
+        vt_tile[d][tp] = (aw[x] & 0xffffu) | (bw[x] << 16);
+        vt_tile[d + 1][tp] = (aw[x] >> 16) | (bw[x] & 0xffff0000u);
+      }
     }
-#pragma unroll
-    for (int g4 = 0; g4 < GP / 4; ++g4)
-      ptile[w][lane][g4] = make_float4(pe[4 * g4], pe[4 * g4 + 1], pe[4 * g4 + 2], pe[4 * g4 + 3]);
     wave_lds_sync();
 
-    // ---- PV: lane owns VPL dims of every TPI-th token ----
+    // ---- O^T += V^T P^T, two 32-token k-steps ----
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int kk = 0; kk < TB / 2; ++kk) {
+      bf16x8 pb;
 #pragma unroll
-      for (int j = 0; j < VPL; ++j) o[g][j] *= alpha[g];
-    const int vlim = nvalid - vt;                       // token slot i is valid iff TPI*i < vlim
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      // keep the weight reads next to their use (hoisting all of them costs registers)
-      if (i % 4 == 0) __builtin_amdgcn_sched_barrier(0);
-      const int r = TPI * i + vt;
-      float vf[VPL];
-      unpack(vreg[i], vf);
-      if (TPI * i < vlim) {} else {                     // rows past the end may hold NaN; weight is 0
-#pragma unroll
-        for (int j = 0; j < VPL; ++j) vf[j] = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        pb[i] = (__bf16)sacc[2 * kk][i];
+        pb[4 + i] = (__bf16)sacc[2 * kk + 1][i];
       }
-      float pw[GP];
+      const int t_lo = 32 * kk + 4 * kg;         // tokens t_lo..+3 and t_lo+16..+3
 #pragma unroll
-      for (int g4 = 0; g4 < GP / 4; ++g4) {
-        const float4 t4 = ptile[w][r][g4];
-        pw[4 * g4] = t4.x; pw[4 * g4 + 1] = t4.y; pw[4 * g4 + 2] = t4.z; pw[4 * g4 + 3] = t4.w;
+      for (int db = 0; db < DB; ++db) {
+        const int d = db * 16 + n;
+        const uint2 lo = *reinterpret_cast<const uint2*>(&vt_tile[d][t_lo / 2]);
+        const uint2 hi = *reinterpret_cast<const uint2*>(&vt_tile[d][(t_lo + 16) / 2]);
+        const uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pb, oacc[db], 0, 0, 0);
       }
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int j = 0; j < VPL; ++j) o[g][j] = fmaf(pw[g], vf[j], o[g][j]);
     }
-    wave_lds_sync();
+    wave_lds_sync();                             // V^T is rewritten by the next tile
+#pragma unroll
+    for (int j = 0; j < NBT; ++j) bts[j] = bts_next[j];
   }
 
-  // ---- combine: token groups inside the wave, then the waves ----
-  float l_tot[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    l_tot[g] = wave_sum(l_part[g]);
-#pragma unroll
-    for (int msk = LPR; msk < kWave; msk *= 2)
-#pragma unroll
-      for (int j = 0; j < VPL; ++j) o[g][j] += __shfl_xor(o[g][j], msk, kWave);
-  }
-  if (lane < LPR) {
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-#pragma unroll
-      for (int j = 0; j < VPL; ++j) sm_o[w][g][vd + j] = o[g][j];
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int g = 0; g < G; ++g) { sm_ml[w][g][0] = m_run[g]; sm_ml[w][g][1] = l_tot[g]; }
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < G * D; e += blockDim.x) {
-    const int g = e / D, d = e % D;
-    float M = -INFINITY;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, sm_ml[ww][g][0]);
-    float O = 0.f, Ls = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      const float f = exp2f(sm_ml[ww][g][0] - M);   // 0 for a wave without tokens
-      Ls = fmaf(f, sm_ml[ww][g][1], Ls);
-      O = fmaf(f, sm_o[ww][g][d], O);
-    }
-    const int qh = h * G + g;
+  // ---- finish: lane (kg, n) holds dims db*16 + 4kg + i of head n ----
+  float l_tot = l_part + __shfl_xor(l_part, 16, kWave);
+  l_tot += __shfl_xor(l_tot, 32, kWave);
+  if (n < G) {
+    const int qh = h * G + n;
     if (nsplit == 1) {
-      p.out[((size_t)row0 * Hq + qh) * D + d] = f32_to_bf16_rne(O / Ls);
+      const float inv = 1.f / l_tot;
+      uint16_t* op = p.out + ((size_t)row0 * Hq + qh) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const uint32_t w0 = (uint32_t)f32_to_bf16_rne(oacc[db][0] * inv) | ((uint32_t)f32_to_bf16_rne(oacc[db][1] * inv) << 16);
+        const uint32_t w1 = (uint32_t)f32_to_bf16_rne(oacc[db][2] * inv) | ((uint32_t)f32_to_bf16_rne(oacc[db][3] * inv) << 16);
+        *reinterpret_cast<uint2*>(op + db * 16 + 4 * kg) = make_uint2(w0, w1);
+      }
     } else {
       const size_t idx = ((size_t)s * Hq + qh) * p.max_splits + split;
-      p.ws_o[idx * D + d] = O;
-      if (d == 0) { p.ws_m[idx] = M; p.ws_l[idx] = Ls; }
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<float4*>(p.ws_o + idx * D + db * 16 + 4 * kg) =
+            make_float4(oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]);
+      if (kg == 0) { p.ws_m[idx] = m_run; p.ws_l[idx] = l_tot; }
     }
   }
 }
@@ -268,7 +292,7 @@ __global__ __launch_bounds__(D) void merge_kernel(AttnParams p) {
   for (int j = 0; j < nsplit; ++j) M = fmaxf(M, p.ws_m[base + j]);
   float O = 0.f, Ls = 0.f;
   for (int j = 0; j < nsplit; ++j) {
-    const float f = exp2f(p.ws_m[base + j] - M);
+    const float f = fast_exp2(p.ws_m[base + j] - M);
     Ls = fmaf(f, p.ws_l[base + j], Ls);
     O = fmaf(f, p.ws_o[(base + j) * D + d], O);
   }
@@ -278,7 +302,7 @@ __global__ __launch_bounds__(D) void merge_kernel(AttnParams p) {
 template <int D, int G, int BS>
 hipError_t launch_decode_t(const AttnParams& p, hipStream_t stream) {
   dim3 grid(p.max_splits, p.Hkv, p.num_seqs);
-  hipLaunchKernelGGL((decode_split_kernel<D, G, BS>), grid, dim3(kWaves * kWave), 0, stream, p);
+  hipLaunchKernelGGL((decode_split_kernel<D, G, BS>), grid, dim3(kWave), 0, stream, p);
   return hipGetLastError();
 }
 
