@@ -56,7 +56,9 @@ void decode_split_kernel(AttnParams p) {
 
   __shared__ __attribute__((aligned(16))) uint32_t vt_tile[D][kVT / 2];
 
-  const int split = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  // KV heads vary fastest across workgroups: the heads of one split read the same pool
+  // rows (heads are interleaved in a slot), so they are dispatched together.
+  const int h = blockIdx.x, split = blockIdx.y, s = blockIdx.z;
   const int row0 = p.qsl[s];
   if (p.qsl[s + 1] - row0 != 1) return;          // not a decode row
   if (row0 < 0 || row0 >= p.num_q_tokens) return;
@@ -301,7 +303,7 @@ __global__ __launch_bounds__(D) void merge_kernel(AttnParams p) {
 
 template <int D, int G, int BS>
 hipError_t launch_decode_t(const AttnParams& p, hipStream_t stream) {
-  dim3 grid(p.max_splits, p.Hkv, p.num_seqs);
+  dim3 grid(p.Hkv, p.max_splits, p.num_seqs);
   hipLaunchKernelGGL((decode_split_kernel<D, G, BS>), grid, dim3(kWave), 0, stream, p);
   return hipGetLastError();
 }
