@@ -157,8 +157,8 @@ PKV_API int kv_append(const void* k_new, const void* v_new, const int64_t* slot_
  *                  written to *workspace_bytes and nothing is enqueued.
  *                  Otherwise *workspace_bytes is the size of the buffer the
  *                  caller passes (PKV_EWORKSPACE if smaller than required).
- *                  The size depends only on num_seqs, num_q_heads, head_dim,
- *                  max_blocks_per_seq and block_size.  The buffer needs no
+ *                  The size depends only on num_seqs, num_q_heads,
+ *                  num_kv_heads, head_dim, max_blocks_per_seq and block_size.  The buffer needs no
  *                  initialisation and must not be shared by calls that can
  *                  run concurrently.
  *   stream         hipStream_t.

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "kernels.h"
 #include "pagedkv.h"
 
@@ -17,21 +19,27 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  int max_splits;
-  size_t o_off, m_off, l_off, total;
+  int64_t max_splits;
+  int64_t plan_capacity;
+  size_t o_off, m_off, l_off, count_off, items_off, total;
 };
 
-WsLayout workspace_layout(int num_seqs, int Hq, int D, int max_blocks, int bs) {
+// Split-K partials of decode rows, then the prefill planner's count and work list.
+// Depends only on (num_seqs, Hq, Hkv, D, max_blocks, bs), so a caller can size it once.
+WsLayout workspace_layout(int num_seqs, int Hq, int Hkv, int D, int max_blocks, int bs) {
   WsLayout w{};
   const int64_t max_tokens = (int64_t)max_blocks * bs;
-  w.max_splits = (int)((max_tokens + kSplitTokens - 1) / kSplitTokens);
+  w.max_splits = (max_tokens + kSplitTokens - 1) / kSplitTokens;
   if (w.max_splits < 1) w.max_splits = 1;
+  const int rows = pkv::kPrefillPairs / (Hq / Hkv);
+  w.plan_capacity = (int64_t)num_seqs * ((max_tokens + rows - 1) / rows);
   const size_t cells = (size_t)num_seqs * Hq * w.max_splits;
   w.o_off = 0;
   w.m_off = round_up(cells * D * sizeof(float), 256);
   w.l_off = w.m_off + round_up(cells * sizeof(float), 256);
-  w.total = w.l_off + round_up(cells * sizeof(float), 256);
-  if (w.total == 0) w.total = 256;
+  w.count_off = w.l_off + round_up(cells * sizeof(float), 256);
+  w.items_off = w.count_off + 256;
+  w.total = w.items_off + round_up((size_t)w.plan_capacity * 8, 256);
   return w;
 }
 
@@ -96,7 +104,8 @@ int paged_attention(void* out, const void* q, const void* k_cache, const void* v
   if (!pkv::decode_supported(head_dim, G, block_size) || !pkv::prefill_supported(head_dim, G, block_size))
     return PKV_EUNSUPPORTED;
   if (num_seqs > 65535 || num_q_heads > 65535) return PKV_EUNSUPPORTED;   // grid y/z limits
-  const WsLayout ws = workspace_layout(num_seqs, num_q_heads, head_dim, max_blocks_per_seq, block_size);
+  const WsLayout ws = workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size);
+  if (ws.max_splits > 65535 || ws.plan_capacity > INT32_MAX) return PKV_EUNSUPPORTED;
   if (!workspace) {
     *workspace_bytes = ws.total;
     return PKV_OK;
@@ -134,6 +143,16 @@ int paged_attention(void* out, const void* q, const void* k_cache, const void* v
   p.ws_o = (float*)(wsb + ws.o_off);
   p.ws_m = (float*)(wsb + ws.m_off);
   p.ws_l = (float*)(wsb + ws.l_off);
+  p.plan_count = (int*)(wsb + ws.count_off);
+  p.plan_items = (int2*)(wsb + ws.items_off);
+  p.plan_capacity = (int)ws.plan_capacity;
+  {
+    // bound on the prefill items of this call: sum over sequences with q_s > 1 of
+    // ceil(q_s / rows) <= num_q_tokens / rows + (number of such sequences)
+    const int rows = pkv::kPrefillPairs / G;
+    const int64_t bound = (num_q_tokens + rows - 1) / rows + std::min<int64_t>(num_seqs, num_q_tokens / 2);
+    p.plan_stride = (int)std::min<int64_t>(bound, ws.plan_capacity);
+  }
 
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = pkv::launch_decode(p, st);

@@ -280,9 +280,20 @@ void decode_split_kernel(AttnParams p) {
 
 // Log-sum-exp merge of the splits of one (decode sequence, query head):
 // out = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j with M = max_j m_j.
+// 256 threads: thread t owns 4 dims (one float4 of every partial) and every
+// SL-th split, so SL partial rows are in flight at once; the SL partial sums
+// are then added through LDS.
+constexpr int kMergeThreads = 256;
+
 template <int D>
-__global__ __launch_bounds__(D) void merge_kernel(AttnParams p) {
-  const int s = blockIdx.x, qh = blockIdx.y, d = threadIdx.x;
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
+  constexpr int LPD = D / 4;                     // threads per partial row
+  constexpr int SL = kMergeThreads / LPD;        // split lanes
+  __shared__ float4 part[SL][LPD];
+  __shared__ float red[kMergeThreads / kWave];
+  __shared__ float lpart[SL];
+
+  const int qh = blockIdx.x, s = blockIdx.y;
   const int row0 = p.qsl[s];
   if (p.qsl[s + 1] - row0 != 1) return;
   if (row0 < 0 || row0 >= p.num_q_tokens) return;
@@ -290,15 +301,45 @@ __global__ __launch_bounds__(D) void merge_kernel(AttnParams p) {
   const int nsplit = (L + p.split_tokens - 1) / p.split_tokens;
   if (nsplit <= 1) return;                       // written directly by the split kernel
   const size_t base = ((size_t)s * p.Hq + qh) * p.max_splits;
+  const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+
+  // M = max_j m_j
   float M = -INFINITY;
-  for (int j = 0; j < nsplit; ++j) M = fmaxf(M, p.ws_m[base + j]);
-  float O = 0.f, Ls = 0.f;
-  for (int j = 0; j < nsplit; ++j) {
+  for (int j = t; j < nsplit; j += kMergeThreads) M = fmaxf(M, p.ws_m[base + j]);
+  M = wave_max(M);
+  if (lane == 0) red[w] = M;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kMergeThreads / kWave; ++i) M = fmaxf(M, red[i]);
+
+  const int sl = t / LPD, dq = t % LPD;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float ls = 0.f;
+#pragma unroll 4
+  for (int j = sl; j < nsplit; j += SL) {
     const float f = fast_exp2(p.ws_m[base + j] - M);
-    Ls = fmaf(f, p.ws_l[base + j], Ls);
-    O = fmaf(f, p.ws_o[(base + j) * D + d], O);
+    const float4 o = *reinterpret_cast<const float4*>(p.ws_o + (base + j) * D + 4 * dq);
+    acc.x = fmaf(f, o.x, acc.x); acc.y = fmaf(f, o.y, acc.y);
+    acc.z = fmaf(f, o.z, acc.z); acc.w = fmaf(f, o.w, acc.w);
+    ls = fmaf(f, p.ws_l[base + j], ls);
   }
-  p.out[((size_t)row0 * p.Hq + qh) * D + d] = f32_to_bf16_rne(O / Ls);
+  part[sl][dq] = acc;
+  if (dq == 0) lpart[sl] = ls;
+  __syncthreads();
+  if (t < LPD) {
+    float4 o = part[0][t];
+    float l = lpart[0];
+#pragma unroll
+    for (int i = 1; i < SL; ++i) {
+      const float4 q4 = part[i][t];
+      o.x += q4.x; o.y += q4.y; o.z += q4.z; o.w += q4.w;
+      l += lpart[i];
+    }
+    const float inv = 1.f / l;
+    const uint32_t w0 = (uint32_t)f32_to_bf16_rne(o.x * inv) | ((uint32_t)f32_to_bf16_rne(o.y * inv) << 16);
+    const uint32_t w1 = (uint32_t)f32_to_bf16_rne(o.z * inv) | ((uint32_t)f32_to_bf16_rne(o.w * inv) << 16);
+    *reinterpret_cast<uint2*>(p.out + ((size_t)row0 * p.Hq + qh) * D + 4 * t) = make_uint2(w0, w1);
+  }
 }
 
 template <int D, int G, int BS>
@@ -344,9 +385,9 @@ hipError_t launch_decode(const AttnParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_merge(const AttnParams& p, hipStream_t stream) {
-  dim3 grid(p.num_seqs, p.Hq);
-  if (p.D == 128) hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(128), 0, stream, p);
-  else if (p.D == 64) hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(64), 0, stream, p);
+  dim3 grid(p.Hq, p.num_seqs);
+  if (p.D == 128) hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kMergeThreads), 0, stream, p);
+  else if (p.D == 64) hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kMergeThreads), 0, stream, p);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

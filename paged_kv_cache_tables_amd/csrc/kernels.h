@@ -27,7 +27,14 @@ struct AttnParams {
   float* ws_o;                    // [num_seqs, Hq, max_splits, D]  unnormalised partial outputs
   float* ws_m;                    // [num_seqs, Hq, max_splits]     partial max (exp2 domain)
   float* ws_l;                    // [num_seqs, Hq, max_splits]     partial sum of exponentials
+  int2* plan_items;               // prefill work list (sequence, row tile), written by the planner
+  int* plan_count;                // number of valid items
+  int plan_capacity;              // items the workspace holds
+  int plan_stride;                // host bound on the items of this call (grid = Hkv * stride)
 };
+
+// Query rows packed into one prefill workgroup (with all G heads of each row).
+constexpr int kPrefillPairs = 128;
 
 hipError_t launch_append(const void* k_new, const void* v_new, const int64_t* slots, int64_t num_tokens,
                          void* k_cache, void* v_cache, int64_t num_slots, int row_chunks,

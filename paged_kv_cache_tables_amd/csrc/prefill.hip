@@ -25,6 +25,13 @@
 //   * K/V tiles are 64 keys, gathered from the paged pool block by block.
 //   * Keys past the sequence end are zero-filled in LDS (V especially: a
 //     masked weight of 0 times a NaN in an unused slot would poison the sum).
+//   * Software pipeline: the next K/V tile is loaded into registers while the
+//     current one is multiplied out of LDS.
+//   * A one-block planner kernel lists the (sequence, row tile) items of the
+//     prefill sequences in the workspace (later row tiles first: they see the
+//     most keys), so no workgroup is launched for decode rows; workgroup ids
+//     are remapped so that consecutive items of one (sequence, KV head) run on
+//     the same XCD and share its L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -35,8 +42,58 @@ namespace {
 constexpr int kWavesP = 4;
 constexpr int kPairsPerWave = 32;
 constexpr int kPairsPerBlock = kWavesP * kPairsPerWave;   // 128
+static_assert(kPairsPerBlock == kPrefillPairs, "planner and kernel agree on the row tile");
 constexpr int kKT = 64;                                    // keys per tile
 constexpr int kVTRow = kKT + 4;                            // padded row of the transposed V tile
+
+// Lists the prefill work items (sequence, row tile) of one call: a sequence
+// with q_s > 1 rows has ceil(q_s / rows_per_tile) row tiles, emitted last tile
+// first.  One block; sequences are scanned in chunks of the block size.
+constexpr int kPlanThreads = 1024;
+
+__global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(const int32_t* __restrict__ qsl, int num_seqs,
+                                                                    int rows_per_tile, int2* __restrict__ items,
+                                                                    int* __restrict__ count, int capacity) {
+  __shared__ int wave_tot[kPlanThreads / kWave];
+  __shared__ int base_sh;
+  const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
+  if (t == 0) base_sh = 0;
+  __syncthreads();
+  for (int s0 = 0; s0 < num_seqs; s0 += kPlanThreads) {
+    const int s = s0 + t;
+    int nt = 0;
+    if (s < num_seqs) {
+      const int q = qsl[s + 1] - qsl[s];
+      if (q > 1) nt = (q + rows_per_tile - 1) / rows_per_tile;
+    }
+    // inclusive scan inside the wave, then across waves
+    int incl = nt;
+#pragma unroll
+    for (int d = 1; d < kWave; d *= 2) {
+      const int y = __shfl_up(incl, d, kWave);
+      if (lane >= d) incl += y;
+    }
+    if (lane == kWave - 1) wave_tot[w] = incl;
+    __syncthreads();
+    int before = base_sh;
+    for (int i = 0; i < w; ++i) before += wave_tot[i];
+    const int off = before + incl - nt;
+    for (int k = 0; k < nt; ++k)
+      if (off + k < capacity) items[off + k] = make_int2(s, nt - 1 - k);
+    __syncthreads();
+    if (t == kPlanThreads - 1) base_sh = off + nt;
+    __syncthreads();
+  }
+  if (t == 0) *count = min(base_sh, capacity);
+}
+
+// Workgroup ids are handed to the 8 XCDs round-robin (id % 8).  This maps them
+// to logical ids so that XCD x runs the contiguous logical range
+// [x * n / 8, (x + 1) * n / 8); n is a multiple of 8.
+__device__ __forceinline__ int xcd_logical_id(int id, int n) {
+  constexpr int kXcd = 8;
+  return (id % kXcd) * (n / kXcd) + id / kXcd;
+}
 
 template <int D, int G>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnParams p) {
@@ -48,7 +105,12 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnParams p) {
   __shared__ uint4 ks_tile[kKT][CH];                    // K tile, row-major, chunk-swizzled
   __shared__ __attribute__((aligned(16))) uint32_t vt_tile[D][kVTRow / 2];   // V^T tile, bf16 pairs along keys
 
-  const int mt = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  // logical id -> (KV head, work item); items past the planner's count do nothing
+  const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
+  const int h = lid / p.plan_stride, item = lid % p.plan_stride;
+  if (h >= p.Hkv || item >= *p.plan_count || item >= p.plan_capacity) return;
+  const int2 it = p.plan_items[item];
+  const int s = it.x, mt = it.y;
   const int row0 = p.qsl[s];
   const int qn = p.qsl[s + 1] - row0;
   if (qn <= 1) return;                           // decode rows are handled elsewhere
@@ -105,50 +167,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnParams p) {
   float m_run = -INFINITY, l_part = 0.f;
   const float c = p.scale_log2;
 
-  for (int kb = 0; kb < key_end; kb += kKT) {
-    __syncthreads();   // the previous tile has been consumed by every wave
-    // ---- stage K (row-major, swizzled) and V (transposed) ----
-    // K: 64 rows x CH chunks; thread handles chunks tid, tid+256, ...
-#pragma unroll
-    for (int e = tid; e < kKT * CH; e += 256) {
-      const int r = e / CH, cc = e % CH;
-      const int tok = kb + r;
-      uint4 val = make_uint4(0u, 0u, 0u, 0u);
-      if (tok < key_end) {
-        const int blk = bt_row[tok / BS];
-        if ((unsigned)blk < (unsigned)p.num_blocks)
-          val = *reinterpret_cast<const uint4*>(kbase + ((size_t)blk * BS + tok % BS) * row_stride + cc * 8);
-      }
-      ks_tile[r][cc ^ (r % CH)] = val;
-    }
-    // V: key pairs (2r, 2r+1) x chunk cc -> 8 dwords of V^T
-#pragma unroll
-    for (int e = tid; e < (kKT / 2) * CH; e += 256) {
-      const int r2 = e / CH, cc = e % CH;
-      const int t0 = kb + 2 * r2, t1 = t0 + 1;
-      uint4 a = make_uint4(0u, 0u, 0u, 0u), b = make_uint4(0u, 0u, 0u, 0u);
-      if (t0 < key_end) {
-        const int blk = bt_row[t0 / BS];
-        if ((unsigned)blk < (unsigned)p.num_blocks)
-          a = *reinterpret_cast<const uint4*>(vbase + ((size_t)blk * BS + t0 % BS) * row_stride + cc * 8);
-      }
-      if (t1 < key_end) {
-        const int blk = bt_row[t1 / BS];
-        if ((unsigned)blk < (unsigned)p.num_blocks)
-          b = *reinterpret_cast<const uint4*>(vbase + ((size_t)blk * BS + t1 % BS) * row_stride + cc * 8);
-      }
-      const uint32_t aw[4] = {a.x, a.y, a.z, a.w};
-      const uint32_t bw[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int d = cc * 8 + 2 * x;
-        vt_tile[d][r2] = (aw[x] & 0xffffu) | (bw[x] << 16);
-        vt_tile[d + 1][r2] = (aw[x] >> 16) | (bw[x] & 0xffff0000u);
-      }
-    }
-    __syncthreads();
-
-    if (!wave_active || kb > wave_lim_max) continue;   // nothing unmasked for this wave
+  auto tile_compute = [&](int kb) {
+    if (!wave_active || kb > wave_lim_max) return;     // nothing unmasked for this wave
 
     // ---- S^T = K Q^T for the two 32-key halves of the tile ----
     floatx16 sacc[2];
@@ -183,14 +203,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnParams p) {
       }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
     const float mn = fmaxf(m_run, tmax);        // finite: key 0 of the first tile is visible to all
-    const float alpha = exp2f(m_run - mn);
+    const float alpha = fast_exp2(m_run - mn);
     m_run = mn;
     float psum = 0.f;
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float e = exp2f(sacc[hf][i] - mn);   // exp2(-inf) = 0 for masked keys
+        const float e = fast_exp2(sacc[hf][i] - mn);   // 2^-inf = 0 for masked keys
         sacc[hf][i] = e;
         psum += e;
       }
@@ -218,8 +238,76 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnParams p) {
                                                            0, 0, 0);
       }
     }
-  }
+    };
 
+  // ---- tile staging: global -> registers (prefetch) -> LDS ----
+  constexpr int NK = kKT * CH / 256;             // K chunks per thread
+  constexpr int NV = (kKT / 2) * CH / 256;       // V (key pair, chunk) items per thread
+  uint4 kpre[NK], vpa[NV], vpb[NV];
+  auto load_tile = [&](int kb) {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int e = tid + 256 * i, r = e / CH, cc = e % CH, tok = kb + r;
+      uint4 val = make_uint4(0u, 0u, 0u, 0u);
+      if (tok < key_end) {
+        const int blk = bt_row[tok / BS];
+        if ((unsigned)blk < (unsigned)p.num_blocks)
+          val = *reinterpret_cast<const uint4*>(kbase + ((size_t)blk * BS + tok % BS) * row_stride + cc * 8);
+      }
+      kpre[i] = val;
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = tid + 256 * i, r2 = e / CH, cc = e % CH;
+      const int t0 = kb + 2 * r2, t1 = t0 + 1;
+      uint4 a = make_uint4(0u, 0u, 0u, 0u), b = make_uint4(0u, 0u, 0u, 0u);
+      if (t0 < key_end) {
+        const int blk = bt_row[t0 / BS];
+        if ((unsigned)blk < (unsigned)p.num_blocks)
+          a = *reinterpret_cast<const uint4*>(vbase + ((size_t)blk * BS + t0 % BS) * row_stride + cc * 8);
+      }
+      if (t1 < key_end) {
+        const int blk = bt_row[t1 / BS];
+        if ((unsigned)blk < (unsigned)p.num_blocks)
+          b = *reinterpret_cast<const uint4*>(vbase + ((size_t)blk * BS + t1 % BS) * row_stride + cc * 8);
+      }
+      vpa[i] = a;
+      vpb[i] = b;
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int e = tid + 256 * i, r = e / CH, cc = e % CH;
+      ks_tile[r][cc ^ (r % CH)] = kpre[i];
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = tid + 256 * i, r2 = e / CH, cc = e % CH;
+      const uint32_t aw[4] = {vpa[i].x, vpa[i].y, vpa[i].z, vpa[i].w};
+      const uint32_t bw[4] = {vpb[i].x, vpb[i].y, vpb[i].z, vpb[i].w};
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int d = cc * 8 + 2 * x;
+        vt_tile[d][r2] = (aw[x] & 0xffffu) | (bw[x] << 16);
+        vt_tile[d + 1][r2] = (aw[x] >> 16) | (bw[x] & 0xffff0000u);
+      }
+    }
+  };
+
+  load_tile(0);
+  store_tile();
+  __syncthreads();
+  for (int kb = 0; kb < key_end; kb += kKT) {
+    const bool has_next = kb + kKT < key_end;
+    if (has_next) load_tile(kb + kKT);           // in flight while this tile is multiplied
+    tile_compute(kb);
+    __syncthreads();                             // every wave is done with this tile
+    if (has_next) {
+      store_tile();
+      __syncthreads();
+    }
+  }
   // ---- finish: O / l, bf16 out ----
   if (!pair_valid) return;
   const float l_tot = l_part + __shfl_xor(l_part, 32, kWave);
@@ -242,7 +330,13 @@ template <int D>
 hipError_t dispatch_g(const AttnParams& p, hipStream_t stream) {
   const int G = p.Hq / p.Hkv;
   const int rows = kPairsPerBlock / G;
-  dim3 grid((p.max_query_len + rows - 1) / rows, p.Hkv, p.num_seqs);
+  hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p.qsl, p.num_seqs, rows,
+                     p.plan_items, p.plan_count, p.plan_capacity);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // one workgroup per (KV head, possible item); rounded up to the 8 XCDs
+  const int64_t n = ((int64_t)p.Hkv * p.plan_stride + 7) / 8 * 8;
+  dim3 grid((unsigned)n);
   switch (G) {
     case 1: hipLaunchKernelGGL((prefill_kernel<D, 1>), grid, dim3(256), 0, stream, p); break;
     case 2: hipLaunchKernelGGL((prefill_kernel<D, 2>), grid, dim3(256), 0, stream, p); break;
