@@ -19,17 +19,24 @@
 // accumulation and the vector ALUs are left with the softmax.
 //
 // Layout (gfx950, one 64-lane wave per workgroup, v_mfma_f32_16x16x32_bf16):
-//   grid = (split, kv head, sequence); the wave walks the split's 64-token tiles.
-//   * Scores transposed, S^T = K Q^T: A = K rows (16 tokens x 32 dims per
-//     MFMA: each lane loads 16 contiguous bytes of one row straight from the
-//     pool), B = the G query rows (heads padded to 16 columns, loaded once).
-//     Each lane's accumulator column is one head, so the per-head max and sum
-//     over the tile need a local reduction plus two lane exchanges.
+//   grid = (kv head, split, sequence), KV heads fastest: the heads of one split
+//   read the same pool rows (heads are interleaved in a slot) close in time.
+//   The wave walks the split's 64-token tiles.
+//   * Loads are fully coalesced: 16 lanes read one 256-byte row (16 bytes each),
+//     4 rows per instruction; the pool block of each instruction is
+//     wave-uniform (scalar base).  K and V of a tile arrive in registers.
+//   * Both tiles pass through one per-wave LDS buffer, row-major with a XOR
+//     swizzle of the 16-byte chunks (row r's chunk c sits at c ^ (r % CH)):
+//     first K, read back as MFMA A operands (16 contiguous bytes per lane,
+//     conflict-free), then V, read back transposed with ds_read_b64_tr_b16.
+//   * Scores transposed, S^T = K Q^T: A = 16 key rows x 32 dims, B = the G
+//     query rows (heads padded to 16 columns, loaded once).  Each lane's
+//     accumulator column is one head: the per-head max and sum need a local
+//     reduction plus two lane exchanges.
 //   * Output transposed, O^T = V^T P^T: B = P^T is the score accumulator
-//     converted to bf16 in place; A = V^T comes from an LDS copy of the V
-//     tile stored transposed ([dim][token], bf16 pairs along tokens).
-//   * The next tile's K loads go out as soon as this tile's QK products have
-//     consumed the K registers; V loads are issued with K at the tile start.
+//     rounded to bf16 in place; A = V^T.
+//   * Streaming: each register set is refilled with the next tile as soon as
+//     its contents are in LDS, so K and V both run one tile ahead.
 //   A sequence with one split writes bf16 output directly, otherwise fp32
 //   partials (O, m, l) go to the workspace for the merge kernel.
 #include "common.h"
@@ -40,21 +47,25 @@ namespace pkv {
 namespace {
 
 constexpr int kTile = 64;        // tokens per tile
-constexpr int kVT = kTile + 4;   // padded row (in tokens) of the transposed V tile
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) short4v lds_short4;
 
 template <int D, int G, int BS>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void decode_split_kernel(AttnParams p) {
   constexpr int CH = D / 8;              // 16-byte chunks per row
+  constexpr int RPI = kWave / CH;        // rows per wave-wide load (4 at d 128)
+  constexpr int NL = kTile / RPI;        // loads per lane per tile, for K and for V
   constexpr int KS = D / 32;             // k-steps of QK (32 dims each)
   constexpr int DB = D / 16;             // 16-dim blocks of the output
   constexpr int TB = kTile / 16;         // 16-token blocks of a tile
   constexpr int NBT = kTile / BS;        // pool blocks spanned by a tile
-  constexpr int NVI = (kTile / 2) * CH / kWave;   // (token pair, chunk) items per lane
   static_assert(G <= 16, "a GQA group is one 16-column MFMA tile");
-  static_assert(kTile % BS == 0, "tiles start on block boundaries");
+  static_assert(kTile % BS == 0 && BS % RPI == 0, "a wave-wide load stays inside one pool block");
 
-  __shared__ __attribute__((aligned(16))) uint32_t vt_tile[D][kVT / 2];
+  __shared__ __attribute__((aligned(16))) uint4 tile[kTile][CH];   // K, then V, of the current tile
 
   // KV heads vary fastest across workgroups: the heads of one split read the same pool
   // rows (heads are interleaved in a slot), so they are dispatched together.
@@ -80,6 +91,7 @@ void decode_split_kernel(AttnParams p) {
   const size_t blk_bytes = (size_t)BS * row_stride * 2;
   const uint32_t row_bytes = (uint32_t)(row_stride * 2);
   const float c = p.scale_log2;
+  const int lrow = lane / CH, lch = lane % CH;   // this lane's row (within a load) and chunk
 
   // ---- Q^T as the B operand: head n, dims ks*32 + kg*8 .. +8 (zero for padding heads) ----
   bf16x8 qreg[KS];
@@ -107,72 +119,65 @@ void decode_split_kernel(AttnParams p) {
       dst[j] = (unsigned)b < (unsigned)nblocks ? b : 0;
     }
   };
-  // Address of tile row r0 + rl, where r0 (a compile-time multiple of GROUP) is shared by
-  // the wave and rl < GROUP varies per lane.  When a group of GROUP rows lies inside one
-  // pool block, the block base is wave-uniform (scalar) and the lane adds a 32-bit offset;
-  // otherwise the lane picks its block from the tile's table entries.
-  auto row_addr = [&](const char* base, const int* bb, auto r0c, auto groupc, int rl) -> const char* {
-    constexpr int r0 = decltype(r0c)::value, GROUP = decltype(groupc)::value;
-    if constexpr (GROUP <= BS) {
-      const char* b = base + (size_t)bb[r0 / BS] * blk_bytes + (uint32_t)(r0 % BS) * row_bytes;
-      return b + (uint32_t)rl * row_bytes;
-    } else {
-      int blk = bb[r0 / BS];
+  // Coalesced tile load: load i covers rows RPI*i .. RPI*i + RPI - 1 (one pool block).
+  const uint32_t lane_off = (uint32_t)lrow * row_bytes + (uint32_t)lch * 16;
+  auto issue = [&](const char* base, const int* bb, uint4* reg) {
 #pragma unroll
-      for (int j = 1; j < GROUP / BS; ++j) if (rl / BS == j) blk = bb[r0 / BS + j];
-      return base + (size_t)blk * blk_bytes + (uint32_t)(rl % BS) * row_bytes;
+    for (int i = 0; i < NL; ++i) {
+      const char* b = base + (size_t)bb[(RPI * i) / BS] * blk_bytes + (uint32_t)((RPI * i) % BS) * row_bytes;
+      reg[i] = *reinterpret_cast<const uint4*>(b + lane_off);
     }
   };
-  // K as the A operand: token block tb, lane's row tb*16 + n, dims ks*32 + kg*8.
-  uint4 kreg[TB][KS];
-  auto issue_k = [&](const int* bb) {
-    static_for<TB>([&](auto tbc) {
-      constexpr int tb = decltype(tbc)::value;
-      const uint4* src = reinterpret_cast<const uint4*>(
-          row_addr(kbase, bb, IntC<tb * 16>(), IntC<16>(), n) + kg * 16);
+  // Registers -> LDS, row-major, chunk c of row r at c ^ (r % CH); rows >= nvalid get zeros.
+  auto stage = [&](const uint4* reg, int nvalid) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kreg[tb][ks] = src[ks * 4];
-    });
+    for (int i = 0; i < NL; ++i) {
+      const int r = RPI * i + lrow;
+      uint4 v = reg[i];
+      if (nvalid < kTile && r >= nvalid) v = make_uint4(0u, 0u, 0u, 0u);
+      tile[r][lch ^ (r % CH)] = v;
+    }
   };
 
   const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
   int bts[NBT];
   load_bts(t_begin, bts);
-  issue_k(bts);
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int ts = t_begin + tile * kTile;
+  uint4 kreg[NL], vreg[NL];
+  issue(kbase, bts, kreg);
+  issue(vbase, bts, vreg);
+  for (int tile_i = 0; tile_i < ntiles; ++tile_i) {
+    const int ts = t_begin + tile_i * kTile;
     const int nvalid = min(kTile, t_end - ts);
-    const bool has_next = tile + 1 < ntiles;
-
-    // ---- V tile: item it = (token pair tp, chunk cc), 16 lanes per 256-byte row ----
-    // item it = lane + 64 j = (token pair tp, chunk cc); rows of one j form a group of TPJ
-    constexpr int TPJ = 2 * kWave / CH;          // tokens covered by one j
-    const int vrow = 2 * (lane / CH);            // lane's first row inside the group
-    const int vcc = lane % CH;
-    uint4 va[NVI], vb[NVI];
-    static_for<NVI>([&](auto jc) {
-      constexpr int j = decltype(jc)::value;
-      const char* a = row_addr(vbase, bts, IntC<TPJ * j>(), IntC<TPJ>(), vrow) + vcc * 16;
-      va[j] = *reinterpret_cast<const uint4*>(a);
-      vb[j] = *reinterpret_cast<const uint4*>(a + row_bytes);   // row vrow + 1: same block (BS even)
-    });
+    const bool has_next = tile_i + 1 < ntiles;
     int bts_next[NBT];
 #pragma unroll
     for (int j = 0; j < NBT; ++j) bts_next[j] = 0;
     if (has_next) load_bts(ts + kTile, bts_next);
+
+    // ---- K tile -> LDS; refill the K registers with the next tile ----
+    stage(kreg, nvalid);
+    __builtin_amdgcn_sched_barrier(0);
+    if (has_next) issue(kbase, bts_next, kreg);
+    wave_lds_sync();
 
     // ---- S^T = K Q^T ----
     floatx4 sacc[TB];
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
       sacc[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      const int r = tb * 16 + n;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kreg[tb][ks]), qreg[ks],
-                                                          sacc[tb], 0, 0, 0);
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 kv = tile[r][(ks * 4 + kg) ^ (r % CH)];
+        sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qreg[ks], sacc[tb], 0, 0, 0);
+      }
     }
-    __builtin_amdgcn_sched_barrier(0);           // the next K loads reuse the K registers
-    if (has_next) issue_k(bts_next);
+    wave_lds_sync();                             // K reads done before V overwrites the buffer
+
+    // ---- V tile -> LDS; refill the V registers with the next tile ----
+    stage(vreg, nvalid);
+    __builtin_amdgcn_sched_barrier(0);
+    if (has_next) issue(vbase, bts_next, vreg);
 
     // ---- online softmax for head n over this tile's tokens (exp2 domain) ----
     float tmax = -INFINITY;
@@ -204,32 +209,14 @@ void decode_split_kernel(AttnParams p) {
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) oacc[db][i] *= alpha;
-
-    // ---- V^T into LDS: dword (tp, dim) = bf16 pair (token 2tp, token 2tp+1) ----
-    if (nvalid < kTile) {                        // rows past the end may hold any bits (NaN)
-#pragma unroll
-      for (int j = 0; j < NVI; ++j) {
-        const int tp = (lane + kWave * j) / CH;
-        if (2 * tp >= nvalid) va[j] = make_uint4(0u, 0u, 0u, 0u);
-        if (2 * tp + 1 >= nvalid) vb[j] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < NVI; ++j) {
-      const int it = lane + kWave * j;
-      const int tp = it / CH, cc = it % CH;
-      const uint32_t aw[4] = {va[j].x, va[j].y, va[j].z, va[j].w};
-      const uint32_t bw[4] = {vb[j].x, vb[j].y, vb[j].z, vb[j].w};
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int d = cc * 8 + 2 * x;
-        vt_tile[d][tp] = (aw[x] & 0xffffu) | (bw[x] << 16);
-        vt_tile[d + 1][tp] = (aw[x] >> 16) | (bw[x] & 0xffff0000u);
-      }
-    }
-    wave_lds_sync();
+    wave_lds_sync();                             // V is in LDS
 
     // ---- O^T += V^T P^T, two 32-token k-steps ----
+    // The A operand of lane (dim n, k-group kg) holds tokens t_lo + 0..3 and t_lo + 16..19
+    // (t_lo = 32 kk + 4 kg), matching the score accumulator layout of the B operand.  A
+    // transposing read returns, in lane i of a 16-lane group, element i % 4 of the 8 bytes
+    // addressed by lane 4 j + i / 4 as its element j: lane a of the group therefore points
+    // at token t_lo + a / 4, dims d0 + 4 (a % 4) .. +3.
 #pragma unroll
     for (int kk = 0; kk < TB / 2; ++kk) {
       bf16x8 pb;
@@ -238,17 +225,20 @@ void decode_split_kernel(AttnParams p) {
         pb[i] = (__bf16)sacc[2 * kk][i];
         pb[4 + i] = (__bf16)sacc[2 * kk + 1][i];
       }
-      const int t_lo = 32 * kk + 4 * kg;         // tokens t_lo..+3 and t_lo+16..+3
+      const int tr = 32 * kk + 4 * kg + n / 4;   // token row this lane addresses
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int d = db * 16 + n;
-        const uint2 lo = *reinterpret_cast<const uint2*>(&vt_tile[d][t_lo / 2]);
-        const uint2 hi = *reinterpret_cast<const uint2*>(&vt_tile[d][(t_lo + 16) / 2]);
-        const uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        const int dim = db * 16 + 4 * (n % 4);   // first of the 4 dims this lane addresses
+        const int ch = dim / 8, half = (dim % 8) / 4;
+        const short* lo_p = reinterpret_cast<const short*>(&tile[tr][ch ^ (tr % CH)]) + 4 * half;
+        const short* hi_p = reinterpret_cast<const short*>(&tile[tr + 16][ch ^ ((tr + 16) % CH)]) + 4 * half;
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)lo_p);
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)hi_p);
+        const short8v av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pb, oacc[db], 0, 0, 0);
       }
     }
-    wave_lds_sync();                             // V^T is rewritten by the next tile
+    wave_lds_sync();                             // V reads done before the next K lands
 #pragma unroll
     for (int j = 0; j < NBT; ++j) bts[j] = bts_next[j];
   }
