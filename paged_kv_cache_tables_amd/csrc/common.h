@@ -49,6 +49,14 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// 16-byte global load with the streaming (non-temporal) hint: for data read once,
+// so it does not displace reusable lines from the caches.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream16(const void* ptr) {
+  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 // Wave-uniform copy of a value (lands in a scalar register).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

@@ -125,7 +125,7 @@ void decode_split_kernel(AttnParams p) {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
       const char* b = base + (size_t)bb[(RPI * i) / BS] * blk_bytes + (uint32_t)((RPI * i) % BS) * row_bytes;
-      reg[i] = *reinterpret_cast<const uint4*>(b + lane_off);
+      reg[i] = load_stream16(b + lane_off);
     }
   };
   // Registers -> LDS, row-major, chunk c of row r at c ^ (r % CH); rows >= nvalid get zeros.
