@@ -57,6 +57,15 @@ __device__ __forceinline__ uint4 load_stream16(const void* ptr) {
   return make_uint4(t.x, t.y, t.z, t.w);
 }
 
+// Load of a value that no kernel of the call writes (block tables, lengths), at a
+// wave-uniform address, through the scalar cache: the constant address space lets
+// the compiler use s_load instead of a vector load (which would share vmcnt with
+// the data loads in flight).
+template <typename T>
+__device__ __forceinline__ T load_invariant(const T* ptr) {
+  return *(const __attribute__((address_space(4))) T*)ptr;
+}
+
 // Wave-uniform copy of a value (lands in a scalar register).
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

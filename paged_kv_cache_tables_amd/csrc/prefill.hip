@@ -13,20 +13,31 @@
 // Layout choices for gfx950:
 //   * A workgroup (4 waves) owns 128 (query row, query head) pairs of one KV
 //     head: the G heads of a GQA group are packed into the M dimension, so
-//     each K/V tile is loaded once for all of them.  Wave w owns 32 pairs.
+//     each K/V tile is loaded once for all of them.  Wave w owns 32 pairs (one
+//     32-column MFMA group), which keeps a wave within 256 registers: two
+//     workgroups share a CU, and one wave's softmax overlaps another's MFMAs.
 //   * Scores are computed transposed, S^T = K Q^T (keys x pairs): A = K rows
 //     (16-byte chunks from LDS), B = Q rows (registers, loaded once).  In the
-//     32x32 accumulator each lane then holds one pair's column, so the row
-//     max / row sum need a single cross-lane exchange (lane ^ 32).
+//     32x32 accumulator each lane holds one pair's column, so the row max and
+//     row sum need one exchange between the two half-waves.
 //   * The output is computed transposed too, O^T = V^T P^T: the B operand P^T
-//     is exactly the score accumulator converted to bf16 in place (no LDS
-//     round trip); the A operand V^T is read from an LDS copy of the V tile
-//     that is stored transposed ([dim][key], rows padded to 68 keys).
-//   * K/V tiles are 64 keys, gathered from the paged pool block by block.
-//   * Keys past the sequence end are zero-filled in LDS (V especially: a
-//     masked weight of 0 times a NaN in an unused slot would poison the sum).
-//   * Software pipeline: the next K/V tile is loaded into registers while the
-//     current one is multiplied out of LDS.
+//     is the score accumulator converted to bf16 in place; the A operand V^T
+//     is read from the row-major V tile with ds_read_b64_tr_b16.
+//   * K and V tiles (64 keys) are row-major in LDS with a XOR swizzle of the
+//     16-byte chunks (row r's chunk c sits at c ^ (r % chunks)).  They are
+//     filled by global-to-LDS loads (global_load_lds_dwordx4: no registers,
+//     no LDS write instructions), double buffered: tile t is multiplied while
+//     tile t+1 is in flight, with one barrier per tile.  Block-table entries
+//     are read a tile ahead of the loads that use them.
+//   * Tile rows past the needed keys hold a copy of the last needed key (a
+//     finite value with weight 0), never an unused pool slot: a weight of 0
+//     times a NaN left in such a slot would poison the sum.
+//   * The running max is raised lazily: the output and row sum are rescaled
+//     only when some row's max grows by more than 2^8 (in the exp2 domain).
+//     Until then weights are taken against the stale max and stay below 2^8,
+//     so the result is the same softmax (the common factor cancels in O / l);
+//     only rounding differs, and bf16 keeps its relative precision at any
+//     magnitude.
 //   * A one-block planner kernel lists the (sequence, row tile) items of the
 //     prefill sequences in the workspace (later row tiles first: they see the
 //     most keys), so no workgroup is launched for decode rows; workgroup ids
@@ -40,11 +51,18 @@ namespace pkv {
 namespace {
 
 constexpr int kWavesP = 4;
-constexpr int kPairsPerWave = 32;
-constexpr int kPairsPerBlock = kWavesP * kPairsPerWave;   // 128
+constexpr int kPairGroups = 1;                             // 32-pair MFMA column groups per wave
+constexpr int kPairsPerWave = 32 * kPairGroups;            // 32
+constexpr int kPairsPerBlock = kWavesP * kPairsPerWave;    // 128
+constexpr int kBuf = 2;                                    // K/V tiles resident in LDS
 static_assert(kPairsPerBlock == kPrefillPairs, "planner and kernel agree on the row tile");
 constexpr int kKT = 64;                                    // keys per tile
-constexpr int kVTRow = kKT + 4;                            // padded row of the transposed V tile
+constexpr float kRescaleSlack = 8.f;                       // lazy max: rescale past 2^8 growth
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) short4v lds_short4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 // Lists the prefill work items (sequence, row tile) of one call: a sequence
 // with q_s > 1 rows has ceil(q_s / rows_per_tile) row tiles, emitted last tile
@@ -95,15 +113,49 @@ __device__ __forceinline__ int xcd_logical_id(int id, int n) {
   return (id % kXcd) * (n / kXcd) + id / kXcd;
 }
 
-template <int D, int G>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(AttnParams p) {
-  constexpr int CH = D / 8;          // 16-byte chunks per K/V row
-  constexpr int KS = D / 16;         // k-steps of the QK product
-  constexpr int DT = D / 32;         // 32-wide dim tiles of the output
-  constexpr int ROWS = kPairsPerBlock / G;   // query rows per workgroup
+// s_waitcnt immediate that waits until at most N vector-memory operations of this wave are
+// outstanding (the other counters are left alone).
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
-  __shared__ uint4 ks_tile[kKT][CH];                    // K tile, row-major, chunk-swizzled
-  __shared__ __attribute__((aligned(16))) uint32_t vt_tile[D][kVTRow / 2];   // V^T tile, bf16 pairs along keys
+// Workgroup barrier for LDS hand-over: no memory operation moves across it in the
+// compiler, and unlike __syncthreads() it does not wait for this wave's outstanding
+// global loads (the tiles in flight).  LDS reads before it have been consumed by then.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams p) {
+  constexpr int CH = D / 8;                 // 16-byte chunks per K/V row
+  constexpr int KS = D / 16;                // k-steps of the QK product
+  constexpr int DT = D / 32;                // 32-wide dim tiles of the output
+  constexpr int PG = kPairGroups;
+  constexpr int ROWS = kPairsPerBlock / G;  // query rows per workgroup
+  constexpr int RW = kWave / CH;            // rows per wave-wide load
+  constexpr int RB = kWavesP * RW;          // rows per workgroup-wide load
+  constexpr int NLD = kKT / RB;             // loads per thread per tile, for K and for V
+  static_assert(kKT % RB == 0, "a tile is a whole number of workgroup-wide loads");
+
+  // K and V of kBuf tiles (the one being multiplied and the ones in flight), as distinct
+  // arrays: every access names its buffer at compile time (the tile loop is unrolled by
+  // kBuf), so the compiler can tell a buffer being filled from one being read.
+  __shared__ __attribute__((aligned(16))) uint4 k_lds0[kKT][CH], k_lds1[kKT][CH];
+  __shared__ __attribute__((aligned(16))) uint4 v_lds0[kKT][CH], v_lds1[kKT][CH];
+  static_assert(kBuf == 2, "two buffers declared");
+  auto kbuf = [&](auto b) -> uint4 (*)[CH] {
+    if constexpr (decltype(b)::value == 0) return k_lds0;
+    else return k_lds1;
+  };
+  auto vbuf = [&](auto b) -> uint4 (*)[CH] {
+    if constexpr (decltype(b)::value == 0) return v_lds0;
+    else return v_lds1;
+  };
 
   // logical id -> (KV head, work item); items past the planner's count do nothing
   const int lid = xcd_logical_id(blockIdx.x, gridDim.x);
@@ -117,213 +169,263 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(AttnParams p) {
   const int j0 = mt * ROWS;
   if (j0 >= qn) return;
   if (row0 < 0 || row0 + qn > p.num_q_tokens) return;
-  const int L = min(p.seq_lens[s], p.max_blocks * p.bs);   // clamp a length the table cannot map
+  const int BS = p.bs;                           // a power of two (checked by the host)
+  const int bs_shift = __builtin_ctz(BS);
+  const int L = min(p.seq_lens[s], p.max_blocks * BS);   // clamp a length the table cannot map
   const int prior = L - qn;
   const int j1 = min(j0 + ROWS, qn);
   const int key_end = prior + j1;                // keys [0, key_end) are needed by this block
+  if (key_end <= 0) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int w = uniform(tid / kWave);
   const int Hq = p.Hkv * G;
   const int* bt_row = p.block_tables + (size_t)s * p.max_blocks;
-  const size_t row_stride = (size_t)p.Hkv * D;
-  const uint16_t* kbase = p.k_cache + (size_t)h * D;
-  const uint16_t* vbase = p.v_cache + (size_t)h * D;
-  const int BS = p.bs;
+  const int nblocks = p.num_blocks > 0x7fffffff ? 0x7fffffff : (int)p.num_blocks;
+  const uint32_t row_bytes = (uint32_t)p.Hkv * D * 2;
+  const size_t blk_bytes = (size_t)BS * row_bytes;
+  const char* kbase = reinterpret_cast<const char*>(p.k_cache + (size_t)h * D);
+  const char* vbase = reinterpret_cast<const char*>(p.v_cache + (size_t)h * D);
 
-  // ---- this lane's pair (B-operand column / accumulator column) ----
-  const int n = lane & 31;                       // column inside the wave's 32 pairs
-  const int kg = lane >> 5;                      // k-group: which 8 of each 16-wide k step
-  const int pair = w * kPairsPerWave + n;        // 0..127
-  const int jrow = j0 + pair / G;
-  const int gq = pair % G;
-  const bool pair_valid = jrow < j1;
-  // last key this pair may attend (inclusive); invalid pairs see only key 0
-  const int lim = pair_valid ? prior + jrow : 0;
+  // ---- this lane's pairs (accumulator / B-operand column n of each group) ----
+  const int n = lane & 31;
+  const int kg = lane >> 5;                      // half-wave: k-group of operands, row group of results
+  int lim[PG];                                   // last key each pair attends (inclusive)
+  bool pvalid[PG];
+  int jrow[PG], gq[PG];
+#pragma unroll
+  for (int pg = 0; pg < PG; ++pg) {
+    const int pair = w * kPairsPerWave + pg * 32 + n;
+    jrow[pg] = j0 + pair / G;
+    gq[pg] = pair % G;
+    pvalid[pg] = jrow[pg] < j1;
+    lim[pg] = pvalid[pg] ? prior + jrow[pg] : 0;   // invalid pairs see key 0 only
+  }
   // wave-level bounds of the causal limits (uniform)
   const int wj_lo = j0 + (w * kPairsPerWave) / G;
-  const int wave_lim_min = prior + min(wj_lo, j1 - 1);
-  const int wave_lim_max = prior + min(j0 + (w * kPairsPerWave + kPairsPerWave - 1) / G, j1 - 1);
+  const int wj_hi = j0 + (w * kPairsPerWave + kPairsPerWave - 1) / G;
   const bool wave_active = wj_lo < j1;
+  const int wave_lim_min = prior + min(wj_lo, j1 - 1);
+  const int wave_lim_max = prior + min(wj_hi, j1 - 1);
 
-  // ---- Q as the B operand: 8 consecutive dims per k step ----
-  bf16x8 qreg[KS];
-  {
-    const uint16_t* qp = p.q + ((size_t)(row0 + (pair_valid ? jrow : j0)) * Hq + (size_t)h * G + gq) * D;
+  // ---- Q^T as the B operand: pair column n, dims ks*16 + kg*8 .. +8 ----
+  bf16x8 qreg[PG][KS];
+#pragma unroll
+  for (int pg = 0; pg < PG; ++pg) {
+    const uint16_t* qp = p.q + ((size_t)(row0 + (pvalid[pg] ? jrow[pg] : j0)) * Hq + (size_t)h * G + gq[pg]) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (pair_valid) v = *reinterpret_cast<const uint4*>(qp + ks * 16 + kg * 8);
-      qreg[ks] = __builtin_bit_cast(bf16x8, v);
+      if (pvalid[pg]) v = *reinterpret_cast<const uint4*>(qp + ks * 16 + kg * 8);
+      qreg[pg][ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
 
-  floatx16 oacc[DT];
+  floatx16 oacc[PG][DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
-  float m_run = -INFINITY, l_part = 0.f;
-  const float c = p.scale_log2;
-
-  auto tile_compute = [&](int kb) {
-    if (!wave_active || kb > wave_lim_max) return;     // nothing unmasked for this wave
-
-    // ---- S^T = K Q^T for the two 32-key halves of the tile ----
-    floatx16 sacc[2];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[hf][i] = 0.f;
-      const int r = hf * 32 + n;                     // key row this lane feeds as A
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int cc = ks * 2 + kg;
-        const uint4 kv = ks_tile[r][cc ^ (r % CH)];
-        sacc[hf] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv), qreg[ks],
-                                                           sacc[hf], 0, 0, 0);
-      }
-    }
-
-    // ---- mask, online softmax (exp2 domain) ----
-    const bool need_mask = kb + kKT - 1 > wave_lim_min;
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float v = sacc[hf][i] * c;
-        if (need_mask) {
-          const int key = kb + hf * 32 + 8 * (i / 4) + 4 * kg + (i % 4);
-          if (key > lim) v = -INFINITY;
-        }
-        sacc[hf][i] = v;
-        tmax = fmaxf(tmax, v);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    const float mn = fmaxf(m_run, tmax);        // finite: key 0 of the first tile is visible to all
-    const float alpha = fast_exp2(m_run - mn);
-    m_run = mn;
-    float psum = 0.f;
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = fast_exp2(sacc[hf][i] - mn);   // 2^-inf = 0 for masked keys
-        sacc[hf][i] = e;
-        psum += e;
-      }
-    l_part = l_part * alpha + psum;
+  for (int pg = 0; pg < PG; ++pg)
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+      for (int i = 0; i < 16; ++i) oacc[pg][dt][i] = 0.f;
+  float m_run[PG], l_part[PG];
+#pragma unroll
+  for (int pg = 0; pg < PG; ++pg) { m_run[pg] = -INFINITY; l_part[pg] = 0.f; }
+  const float c = p.scale_log2;
+
+  // ---- tile loads: global -> LDS directly (global_load_lds_dwordx4) ----
+  // Load i of wave w fills rows RB*i + RW*w .. +RW-1 of a tile: 1 KB of LDS written at
+  // base + 16 * lane, so lane (row lrow, slot pc) fetches the chunk that the swizzle puts
+  // there, pc ^ (row % CH).  The rows of one load lie in one pool block (block sizes are
+  // multiples of RW), so its block id is wave-uniform.  Rows at or past key_end fetch
+  // row key_end - 1 instead: finite data that the causal mask gives weight 0.
+  // The table entries of a tile come from one vector load (lane j: block kb / BS + j,
+  // clamped to the last needed block) issued right after the previous tile's loads, so
+  // the wait for that tile covers it; each load then reads its block id with readlane.
+  const int lrow = lane / CH, pc = lane % CH;
+  const int last_blk = (key_end - 1) >> bs_shift;
+  auto fetch_bt = [&](int kb) -> int {
+    return bt_row[min((kb >> bs_shift) + lane, last_blk)];
+  };
+  auto issue = [&](auto b, int kb, int btv) {
+    uint4 (*kd)[CH] = kbuf(b);
+    uint4 (*vd)[CH] = vbuf(b);
+    uint32_t src_row[NLD];
+    size_t blk_off[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int g_tok = kb + RB * i + RW * w;    // first row of load i (wave-uniform)
+      const int tok = min(g_tok, key_end - 1);
+      const int bl = __builtin_amdgcn_readlane(btv, (tok >> bs_shift) - (kb >> bs_shift));
+      blk_off[i] = (size_t)((unsigned)bl < (unsigned)nblocks ? bl : 0) * blk_bytes;   // out-of-pool: block 0
+      src_row[i] = (uint32_t)((tok & (BS - 1)) + min(lrow, max(key_end - 1 - g_tok, 0)));
+    }
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int r = RB * i + RW * w + lrow;      // tile row this lane's chunk belongs to
+      const size_t off = blk_off[i] + src_row[i] * row_bytes + (uint32_t)((pc ^ (r % CH)) * 16);
+      __builtin_amdgcn_global_load_lds(kbase + off, (lds_void*)&kd[RB * i + RW * w][0], 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int r = RB * i + RW * w + lrow;
+      const size_t off = blk_off[i] + src_row[i] * row_bytes + (uint32_t)((pc ^ (r % CH)) * 16);
+      __builtin_amdgcn_global_load_lds(vbase + off, (lds_void*)&vd[RB * i + RW * w][0], 16, 0, 0);
+    }
+  };
+
+  auto tile_compute = [&](auto b, int kb) {
+    uint4 (*kt)[CH] = kbuf(b);
+    uint4 (*vt)[CH] = vbuf(b);
+    // ---- S^T = K Q^T: two 32-key halves x two pair groups ----
+    floatx16 sacc[2][PG];
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int pg = 0; pg < PG; ++pg)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[kh][pg][i] = 0.f;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const int r = kh * 32 + n;                 // key row this lane feeds as A
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 kv = kt[r][(ks * 2 + kg) ^ (r % CH)];
+#pragma unroll
+        for (int pg = 0; pg < PG; ++pg)
+          sacc[kh][pg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv), qreg[pg][ks],
+                                                                 sacc[kh][pg], 0, 0, 0);
+      }
+    }
+
+    // ---- scale, causal mask, tile max (exp2 domain) ----
+    // accumulator element i of half kh holds key kb + 32 kh + 8 (i / 4) + 4 kg + i % 4
+    const bool need_mask = kb + kKT - 1 > wave_lim_min;
+    float m_new[PG];
+    bool grow = false;
+#pragma unroll
+    for (int pg = 0; pg < PG; ++pg) {
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float v = sacc[kh][pg][i] * c;
+          if (need_mask) {
+            const int key = kb + kh * 32 + 8 * (i / 4) + 4 * kg + (i % 4);
+            if (key > lim[pg]) v = -INFINITY;
+          }
+          sacc[kh][pg][i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      const int x = __float_as_int(tmax);
+      const auto sw = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+      tmax = fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));
+      m_new[pg] = fmaxf(m_run[pg], tmax);
+      grow |= m_new[pg] > m_run[pg] + kRescaleSlack;
+    }
+    // ---- lazy rescale: only when some row's max has grown past the slack ----
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int pg = 0; pg < PG; ++pg) {
+        const float alpha = fast_exp2(m_run[pg] - m_new[pg]);   // 0 on the first tile
+        m_run[pg] = m_new[pg];
+        l_part[pg] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[pg][dt][i] *= alpha;
+      }
+    }
+    // ---- weights 2^(s - m) (below 2^8), row sums, bf16 P^T operands ----
+    bf16x8 pb[PG][4];
+#pragma unroll
+    for (int pg = 0; pg < PG; ++pg) {
+      float psum = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float e = fast_exp2(sacc[kk >> 1][pg][(kk & 1) * 8 + j] - m_run[pg]);   // 0 when masked
+          psum += e;
+          pb[pg][kk][j] = (__bf16)e;
+        }
+      l_part[pg] += psum;
+    }
 
     // ---- O^T += V^T P^T over four 16-key steps ----
+    // A operand of lane (dim 32 dt + n, k-group kg): keys 16 kk + 4 kg + 0..3 and +8..+11,
+    // the keys of the B operand's elements.  A transposing read gives lane i of a 16-lane
+    // group element i % 4 of the 8 bytes addressed by lane 4 j + i / 4 as its element j, so
+    // lane a of the group points at key t0 + a / 4, dims dbase + 4 (a % 4) .. +3.
+    const int a16 = lane & 15;
+    const int dsub = 16 * ((lane >> 4) & 1) + 4 * (a16 & 3);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const int hf = kk >> 1, part = kk & 1;
-      bf16x8 pb;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pb[i] = (__bf16)sacc[hf][part * 8 + i];
-      const int key_lo = kk * 16 + 4 * kg;            // keys key_lo..+3 and key_lo+8..+11
+      const int t_lo = 16 * kk + 4 * kg + (a16 >> 2);
+      const int t_hi = t_lo + 8;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int d = dt * 32 + n;
-        const uint2 lo = *reinterpret_cast<const uint2*>(&vt_tile[d][key_lo / 2]);
-        const uint2 hi = *reinterpret_cast<const uint2*>(&vt_tile[d][(key_lo + 8) / 2]);
-        const uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb, oacc[dt],
-                                                           0, 0, 0);
-      }
-    }
-    };
-
-  // ---- tile staging: global -> registers (prefetch) -> LDS ----
-  constexpr int NK = kKT * CH / 256;             // K chunks per thread
-  constexpr int NV = (kKT / 2) * CH / 256;       // V (key pair, chunk) items per thread
-  uint4 kpre[NK], vpa[NV], vpb[NV];
-  auto load_tile = [&](int kb) {
+        const int dim = 32 * dt + dsub;
+        const int ch = dim / 8, half = (dim % 8) / 4;
+        const short* lo_p = reinterpret_cast<const short*>(&vt[t_lo][ch ^ (t_lo % CH)]) + 4 * half;
+        const short* hi_p = reinterpret_cast<const short*>(&vt[t_hi][ch ^ (t_hi % CH)]) + 4 * half;
+        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)lo_p);
+        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)hi_p);
+        const short8v av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int e = tid + 256 * i, r = e / CH, cc = e % CH, tok = kb + r;
-      uint4 val = make_uint4(0u, 0u, 0u, 0u);
-      if (tok < key_end) {
-        const int blk = bt_row[tok / BS];
-        if ((unsigned)blk < (unsigned)p.num_blocks)
-          val = *reinterpret_cast<const uint4*>(kbase + ((size_t)blk * BS + tok % BS) * row_stride + cc * 8);
-      }
-      kpre[i] = val;
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int e = tid + 256 * i, r2 = e / CH, cc = e % CH;
-      const int t0 = kb + 2 * r2, t1 = t0 + 1;
-      uint4 a = make_uint4(0u, 0u, 0u, 0u), b = make_uint4(0u, 0u, 0u, 0u);
-      if (t0 < key_end) {
-        const int blk = bt_row[t0 / BS];
-        if ((unsigned)blk < (unsigned)p.num_blocks)
-          a = *reinterpret_cast<const uint4*>(vbase + ((size_t)blk * BS + t0 % BS) * row_stride + cc * 8);
-      }
-      if (t1 < key_end) {
-        const int blk = bt_row[t1 / BS];
-        if ((unsigned)blk < (unsigned)p.num_blocks)
-          b = *reinterpret_cast<const uint4*>(vbase + ((size_t)blk * BS + t1 % BS) * row_stride + cc * 8);
-      }
-      vpa[i] = a;
-      vpb[i] = b;
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-      const int e = tid + 256 * i, r = e / CH, cc = e % CH;
-      ks_tile[r][cc ^ (r % CH)] = kpre[i];
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      const int e = tid + 256 * i, r2 = e / CH, cc = e % CH;
-      const uint32_t aw[4] = {vpa[i].x, vpa[i].y, vpa[i].z, vpa[i].w};
-      const uint32_t bw[4] = {vpb[i].x, vpb[i].y, vpb[i].z, vpb[i].w};
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int d = cc * 8 + 2 * x;
-        vt_tile[d][r2] = (aw[x] & 0xffffu) | (bw[x] << 16);
-        vt_tile[d + 1][r2] = (aw[x] >> 16) | (bw[x] & 0xffff0000u);
+        for (int pg = 0; pg < PG; ++pg)
+          oacc[pg][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb[pg][kk],
+                                                                 oacc[pg][dt], 0, 0, 0);
       }
     }
   };
 
-  load_tile(0);
-  store_tile();
-  __syncthreads();
-  for (int kb = 0; kb < key_end; kb += kKT) {
-    const bool has_next = kb + kKT < key_end;
-    if (has_next) load_tile(kb + kKT);           // in flight while this tile is multiplied
-    tile_compute(kb);
-    __syncthreads();                             // every wave is done with this tile
-    if (has_next) {
-      store_tile();
-      __syncthreads();
+  // ---- pipeline over tiles: tile t in buffer t % kBuf, the next kBuf - 1 tiles in flight ----
+  // Per thread, a tile is 2 NLD loads (K then V) issued in tile order, so "tile t has
+  // landed" is "at most the loads of the tiles issued after it are outstanding".
+  const int ntiles = (key_end + kKT - 1) / kKT;
+  int btv = fetch_bt(0);
+  issue(IntC<0>(), 0, btv);
+  if (ntiles > 1) btv = fetch_bt(kKT);
+  auto step = [&](auto b, int t) {
+    constexpr int B = decltype(b)::value;
+    const int kb = t * kKT;
+    wait_vmem<0>();                              // this thread's part of tile t (and the next table entries) landed
+    lds_barrier();                               // all of tile t visible; buffer (t+1) % 2 no longer read
+    if (t + 1 < ntiles) {
+      issue(IntC<(B + 1) % kBuf>(), kb + kKT, btv);
+      if (t + 2 < ntiles) btv = fetch_bt(kb + 2 * kKT);
     }
+    if (wave_active && kb <= wave_lim_max) tile_compute(b, kb);
+  };
+  for (int t = 0; t < ntiles; t += kBuf) {
+    step(IntC<0>(), t);
+    if (t + 1 < ntiles) step(IntC<1>(), t + 1);
   }
-  // ---- finish: O / l, bf16 out ----
-  if (!pair_valid) return;
-  const float l_tot = l_part + __shfl_xor(l_part, 32, kWave);
-  const float inv = 1.f / l_tot;
-  uint16_t* op = p.out + ((size_t)(row0 + jrow) * Hq + (size_t)h * G + gq) * D;
+
+  // ---- finish: O / l, bf16 out; lane holds dims 32 dt + 8 q + 4 kg + 0..3 of its pair ----
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int pg = 0; pg < PG; ++pg) {
+    const int x = __float_as_int(l_part[pg]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    const float l_tot = __int_as_float(sw[0]) + __int_as_float(sw[1]);
+    if (!pvalid[pg]) continue;
+    const float inv = 1.f / l_tot;
+    uint16_t* op = p.out + ((size_t)(row0 + jrow[pg]) * Hq + (size_t)h * G + gq[pg]) * D;
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int d = dt * 32 + 8 * q4 + 4 * kg;
-      const uint32_t w0 = (uint32_t)f32_to_bf16_rne(oacc[dt][q4 * 4 + 0] * inv) |
-                          ((uint32_t)f32_to_bf16_rne(oacc[dt][q4 * 4 + 1] * inv) << 16);
-      const uint32_t w1 = (uint32_t)f32_to_bf16_rne(oacc[dt][q4 * 4 + 2] * inv) |
-                          ((uint32_t)f32_to_bf16_rne(oacc[dt][q4 * 4 + 3] * inv) << 16);
-      *reinterpret_cast<uint2*>(op + d) = make_uint2(w0, w1);
-    }
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = dt * 32 + 8 * q4 + 4 * kg;
+        const uint32_t w0 = (uint32_t)f32_to_bf16_rne(oacc[pg][dt][q4 * 4 + 0] * inv) |
+                            ((uint32_t)f32_to_bf16_rne(oacc[pg][dt][q4 * 4 + 1] * inv) << 16);
+        const uint32_t w1 = (uint32_t)f32_to_bf16_rne(oacc[pg][dt][q4 * 4 + 2] * inv) |
+                            ((uint32_t)f32_to_bf16_rne(oacc[pg][dt][q4 * 4 + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(op + d) = make_uint2(w0, w1);
+      }
+  }
 }
 
 template <int D>
@@ -338,11 +440,11 @@ hipError_t dispatch_g(const AttnParams& p, hipStream_t stream) {
   const int64_t n = ((int64_t)p.Hkv * p.plan_stride + 7) / 8 * 8;
   dim3 grid((unsigned)n);
   switch (G) {
-    case 1: hipLaunchKernelGGL((prefill_kernel<D, 1>), grid, dim3(256), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((prefill_kernel<D, 2>), grid, dim3(256), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((prefill_kernel<D, 4>), grid, dim3(256), 0, stream, p); break;
-    case 8: hipLaunchKernelGGL((prefill_kernel<D, 8>), grid, dim3(256), 0, stream, p); break;
-    case 16: hipLaunchKernelGGL((prefill_kernel<D, 16>), grid, dim3(256), 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((prefill_kernel<D, 1>), grid, dim3(kWavesP * kWave), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<D, 2>), grid, dim3(kWavesP * kWave), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<D, 4>), grid, dim3(kWavesP * kWave), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((prefill_kernel<D, 8>), grid, dim3(kWavesP * kWave), 0, stream, p); break;
+    case 16: hipLaunchKernelGGL((prefill_kernel<D, 16>), grid, dim3(kWavesP * kWave), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -351,7 +453,10 @@ hipError_t dispatch_g(const AttnParams& p, hipStream_t stream) {
 }  // namespace
 
 bool prefill_supported(int D, int G, int bs) {
-  return (D == 64 || D == 128) && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16) && bs > 0;
+  // a wave-wide tile load (64 / (D / 8) rows) must stay inside one pool block, and a
+  // tile (64 keys) must hold whole blocks
+  return (D == 64 || D == 128) && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16) &&
+         (bs == 8 || bs == 16 || bs == 32) && bs % (kWave / (D / 8)) == 0;
 }
 
 hipError_t launch_prefill(const AttnParams& p, hipStream_t stream) {
