@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <float.h>
 #include <stdint.h>
 
 #include <type_traits>
@@ -64,6 +65,19 @@ __device__ __forceinline__ uint4 load_stream16(const void* ptr) {
 template <typename T>
 __device__ __forceinline__ T load_invariant(const T* ptr) {
   return *(const __attribute__((address_space(4))) T*)ptr;
+}
+
+// XOR swizzle of the 16-byte chunks of a row-major LDS tile with CH chunks per row
+// (CH = 8 or 16): chunk c of row r sits at c ^ chunk_swizzle<CH>(r).  The LDS serves
+// 256 bytes (64 banks) at a time; the pattern keeps the prefill read shapes
+// conflict-free: one chunk of 16 consecutive rows (MFMA A operands of K), and the
+// transposing reads of V, where 32 lanes cover 4 aligned rows x 4 adjacent chunks.
+// For 256-byte rows: 0 4 8 12 2 6 10 14 1 5 9 13 3 7 11 15 over 16 consecutive rows.
+template <int CH>
+__device__ __forceinline__ int chunk_swizzle(int r) {
+  static_assert(CH == 8 || CH == 16, "rows of 128 or 256 bytes");
+  if constexpr (CH == 16) return 4 * (r & 3) + 2 * ((r >> 2) & 1) + ((r >> 3) & 1);
+  else return (2 * (r & 3) + ((r >> 2) & 1)) & 7;
 }
 
 // Wave-uniform copy of a value (lands in a scalar register).

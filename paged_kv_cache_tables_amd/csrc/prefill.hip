@@ -24,7 +24,8 @@
 //     is the score accumulator converted to bf16 in place; the A operand V^T
 //     is read from the row-major V tile with ds_read_b64_tr_b16.
 //   * K and V tiles (64 keys) are row-major in LDS with a XOR swizzle of the
-//     16-byte chunks (row r's chunk c sits at c ^ (r % chunks)).  They are
+//     16-byte chunks (row r's chunk c sits at c ^ chunk_swizzle(r), which
+//     keeps the K operand reads and the transposing V reads conflict-free).  They are
 //     filled by global-to-LDS loads (global_load_lds_dwordx4: no registers,
 //     no LDS write instructions), double buffered: tile t is multiplied while
 //     tile t+1 is in flight, with one barrier per tile.  Block-table entries
@@ -37,7 +38,8 @@
 //     Until then weights are taken against the stale max and stay below 2^8,
 //     so the result is the same softmax (the common factor cancels in O / l);
 //     only rounding differs, and bf16 keeps its relative precision at any
-//     magnitude.
+//     magnitude.  The row sums add the bf16 weights the MFMA multiplies (two
+//     per v_dot2_f32_bf16), so numerator and denominator see the same values.
 //   * A one-block planner kernel lists the (sequence, row tile) items of the
 //     prefill sequences in the workspace (later row tiles first: they see the
 //     most keys), so no workgroup is launched for decode rows; workgroup ids
@@ -209,6 +211,14 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
   const int wave_lim_min = prior + min(wj_lo, j1 - 1);
   const int wave_lim_max = prior + min(wj_hi, j1 - 1);
 
+  // Scores enter the softmax as c s, c = scale log2(e).  The kernel works with |c| (at
+  // least FLT_MIN, so masked -inf scores stay -inf): for c < 0 the query is negated,
+  // which is exact in bf16, and then max(c s) = |c| max(s) and 2^(c s - m) is one fma
+  // and one exp2 per score.
+  const float c_in = p.scale_log2;
+  const uint32_t qflip = c_in < 0.f ? 0x80008000u : 0u;
+  const float c = fmaxf(fabsf(c_in), FLT_MIN);
+
   // ---- Q^T as the B operand: pair column n, dims ks*16 + kg*8 .. +8 ----
   bf16x8 qreg[PG][KS];
 #pragma unroll
@@ -218,6 +228,7 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
     for (int ks = 0; ks < KS; ++ks) {
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
       if (pvalid[pg]) v = *reinterpret_cast<const uint4*>(qp + ks * 16 + kg * 8);
+      v.x ^= qflip; v.y ^= qflip; v.z ^= qflip; v.w ^= qflip;
       qreg[pg][ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -232,12 +243,11 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
   float m_run[PG], l_part[PG];
 #pragma unroll
   for (int pg = 0; pg < PG; ++pg) { m_run[pg] = -INFINITY; l_part[pg] = 0.f; }
-  const float c = p.scale_log2;
 
   // ---- tile loads: global -> LDS directly (global_load_lds_dwordx4) ----
   // Load i of wave w fills rows RB*i + RW*w .. +RW-1 of a tile: 1 KB of LDS written at
   // base + 16 * lane, so lane (row lrow, slot pc) fetches the chunk that the swizzle puts
-  // there, pc ^ (row % CH).  The rows of one load lie in one pool block (block sizes are
+  // there, pc ^ chunk_swizzle(row).  The rows of one load lie in one pool block (block sizes are
   // multiples of RW), so its block id is wave-uniform.  Rows at or past key_end fetch
   // row key_end - 1 instead: finite data that the causal mask gives weight 0.
   // The table entries of a tile come from one vector load (lane j: block kb / BS + j,
@@ -264,13 +274,13 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int r = RB * i + RW * w + lrow;      // tile row this lane's chunk belongs to
-      const size_t off = blk_off[i] + src_row[i] * row_bytes + (uint32_t)((pc ^ (r % CH)) * 16);
+      const size_t off = blk_off[i] + src_row[i] * row_bytes + (uint32_t)((pc ^ chunk_swizzle<CH>(r)) * 16);
       __builtin_amdgcn_global_load_lds(kbase + off, (lds_void*)&kd[RB * i + RW * w][0], 16, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int r = RB * i + RW * w + lrow;
-      const size_t off = blk_off[i] + src_row[i] * row_bytes + (uint32_t)((pc ^ (r % CH)) * 16);
+      const size_t off = blk_off[i] + src_row[i] * row_bytes + (uint32_t)((pc ^ chunk_swizzle<CH>(r)) * 16);
       __builtin_amdgcn_global_load_lds(vbase + off, (lds_void*)&vd[RB * i + RW * w][0], 16, 0, 0);
     }
   };
@@ -291,7 +301,7 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
       const int r = kh * 32 + n;                 // key row this lane feeds as A
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const uint4 kv = kt[r][(ks * 2 + kg) ^ (r % CH)];
+        const uint4 kv = kt[r][(ks * 2 + kg) ^ chunk_swizzle<CH>(r)];
 #pragma unroll
         for (int pg = 0; pg < PG; ++pg)
           sacc[kh][pg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv), qreg[pg][ks],
@@ -299,7 +309,7 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
       }
     }
 
-    // ---- scale, causal mask, tile max (exp2 domain) ----
+    // ---- causal mask, tile max (exp2 domain: c times the raw maximum) ----
     // accumulator element i of half kh holds key kb + 32 kh + 8 (i / 4) + 4 kg + i % 4
     const bool need_mask = kb + kKT - 1 > wave_lim_min;
     float m_new[PG];
@@ -311,7 +321,7 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float v = sacc[kh][pg][i] * c;
+          float v = sacc[kh][pg][i];
           if (need_mask) {
             const int key = kb + kh * 32 + 8 * (i / 4) + 4 * kg + (i % 4);
             if (key > lim[pg]) v = -INFINITY;
@@ -322,7 +332,7 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
       const int x = __float_as_int(tmax);
       const auto sw = __builtin_amdgcn_permlane32_swap(x, x, false, false);
       tmax = fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));
-      m_new[pg] = fmaxf(m_run[pg], tmax);
+      m_new[pg] = fmaxf(m_run[pg], tmax * c);   // a fully masked column keeps its max
       grow |= m_new[pg] > m_run[pg] + kRescaleSlack;
     }
     // ---- lazy rescale: only when some row's max has grown past the slack ----
@@ -338,19 +348,23 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
           for (int i = 0; i < 16; ++i) oacc[pg][dt][i] *= alpha;
       }
     }
-    // ---- weights 2^(s - m) (below 2^8), row sums, bf16 P^T operands ----
+    // ---- weights 2^(c s - m) (below 2^8), bf16 P^T operands, row sums of the bf16 weights ----
     bf16x8 pb[PG][4];
 #pragma unroll
     for (int pg = 0; pg < PG; ++pg) {
+      const float neg_m = -m_run[pg];
       float psum = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
+      for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float e = fast_exp2(sacc[kk >> 1][pg][(kk & 1) * 8 + j] - m_run[pg]);   // 0 when masked
-          psum += e;
-          pb[pg][kk][j] = (__bf16)e;
-        }
+        for (int j = 0; j < 8; ++j)
+          pb[pg][kk][j] = (__bf16)fast_exp2(fmaf(sacc[kk >> 1][pg][(kk & 1) * 8 + j], c, neg_m));   // 0 when masked
+        const uint4 pw = __builtin_bit_cast(uint4, pb[pg][kk]);
+        psum = dot2_bf16(pw.x, 0x3f803f80u, psum);   // + p0 + p1 (bf16 1.0 pairs)
+        psum = dot2_bf16(pw.y, 0x3f803f80u, psum);
+        psum = dot2_bf16(pw.z, 0x3f803f80u, psum);
+        psum = dot2_bf16(pw.w, 0x3f803f80u, psum);
+      }
       l_part[pg] += psum;
     }
 
@@ -369,8 +383,8 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
       for (int dt = 0; dt < DT; ++dt) {
         const int dim = 32 * dt + dsub;
         const int ch = dim / 8, half = (dim % 8) / 4;
-        const short* lo_p = reinterpret_cast<const short*>(&vt[t_lo][ch ^ (t_lo % CH)]) + 4 * half;
-        const short* hi_p = reinterpret_cast<const short*>(&vt[t_hi][ch ^ (t_hi % CH)]) + 4 * half;
+        const short* lo_p = reinterpret_cast<const short*>(&vt[t_lo][ch ^ chunk_swizzle<CH>(t_lo)]) + 4 * half;
+        const short* hi_p = reinterpret_cast<const short*>(&vt[t_hi][ch ^ chunk_swizzle<CH>(t_hi)]) + 4 * half;
         const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)lo_p);
         const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)hi_p);
         const short8v av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
