@@ -53,8 +53,7 @@ namespace pkv {
 namespace {
 
 constexpr int kWavesP = 4;
-constexpr int kPairGroups = 1;                             // 32-pair MFMA column groups per wave
-constexpr int kPairsPerWave = 32 * kPairGroups;            // 32
+constexpr int kPairsPerWave = 32;                          // one 32-column MFMA group
 constexpr int kPairsPerBlock = kWavesP * kPairsPerWave;    // 128
 constexpr int kBuf = 2;                                    // K/V tiles resident in LDS
 static_assert(kPairsPerBlock == kPrefillPairs, "planner and kernel agree on the row tile");
@@ -137,7 +136,6 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
   constexpr int CH = D / 8;                 // 16-byte chunks per K/V row
   constexpr int KS = D / 16;                // k-steps of the QK product
   constexpr int DT = D / 32;                // 32-wide dim tiles of the output
-  constexpr int PG = kPairGroups;
   constexpr int ROWS = kPairsPerBlock / G;  // query rows per workgroup
   constexpr int RW = kWave / CH;            // rows per wave-wide load
   constexpr int RB = kWavesP * RW;          // rows per workgroup-wide load
@@ -190,20 +188,14 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
   const char* kbase = reinterpret_cast<const char*>(p.k_cache + (size_t)h * D);
   const char* vbase = reinterpret_cast<const char*>(p.v_cache + (size_t)h * D);
 
-  // ---- this lane's pairs (accumulator / B-operand column n of each group) ----
+  // ---- this lane's pair (accumulator / B-operand column n) ----
   const int n = lane & 31;
   const int kg = lane >> 5;                      // half-wave: k-group of operands, row group of results
-  int lim[PG];                                   // last key each pair attends (inclusive)
-  bool pvalid[PG];
-  int jrow[PG], gq[PG];
-#pragma unroll
-  for (int pg = 0; pg < PG; ++pg) {
-    const int pair = w * kPairsPerWave + pg * 32 + n;
-    jrow[pg] = j0 + pair / G;
-    gq[pg] = pair % G;
-    pvalid[pg] = jrow[pg] < j1;
-    lim[pg] = pvalid[pg] ? prior + jrow[pg] : 0;   // invalid pairs see key 0 only
-  }
+  const int pair = w * kPairsPerWave + n;
+  const int jrow = j0 + pair / G;
+  const int gq = pair % G;
+  const bool pvalid = jrow < j1;
+  const int lim = pvalid ? prior + jrow : 0;     // last key this pair attends; invalid pairs see key 0 only
   // wave-level bounds of the causal limits (uniform)
   const int wj_lo = j0 + (w * kPairsPerWave) / G;
   const int wj_hi = j0 + (w * kPairsPerWave + kPairsPerWave - 1) / G;
@@ -220,29 +212,24 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
   const float c = fmaxf(fabsf(c_in), FLT_MIN);
 
   // ---- Q^T as the B operand: pair column n, dims ks*16 + kg*8 .. +8 ----
-  bf16x8 qreg[PG][KS];
-#pragma unroll
-  for (int pg = 0; pg < PG; ++pg) {
-    const uint16_t* qp = p.q + ((size_t)(row0 + (pvalid[pg] ? jrow[pg] : j0)) * Hq + (size_t)h * G + gq[pg]) * D;
+  bf16x8 qreg[KS];
+  {
+    const uint16_t* qp = p.q + ((size_t)(row0 + (pvalid ? jrow : j0)) * Hq + (size_t)h * G + gq) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (pvalid[pg]) v = *reinterpret_cast<const uint4*>(qp + ks * 16 + kg * 8);
+      if (pvalid) v = *reinterpret_cast<const uint4*>(qp + ks * 16 + kg * 8);
       v.x ^= qflip; v.y ^= qflip; v.z ^= qflip; v.w ^= qflip;
-      qreg[pg][ks] = __builtin_bit_cast(bf16x8, v);
+      qreg[ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
 
-  floatx16 oacc[PG][DT];
+  floatx16 oacc[DT];
 #pragma unroll
-  for (int pg = 0; pg < PG; ++pg)
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[pg][dt][i] = 0.f;
-  float m_run[PG], l_part[PG];
-#pragma unroll
-  for (int pg = 0; pg < PG; ++pg) { m_run[pg] = -INFINITY; l_part[pg] = 0.f; }
+    for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
+  float m_run = -INFINITY, l_part = 0.f;
 
   // ---- tile loads: global -> LDS directly (global_load_lds_dwordx4) ----
   // Load i of wave w fills rows RB*i + RW*w .. +RW-1 of a tile: 1 KB of LDS written at
@@ -285,115 +272,124 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
     }
   };
 
+  // Per-lane LDS addressing.  The A operand of the QK product for key half kh and
+  // k-step ks is row 32 kh + n, chunk 2 ks + kg.  The transposing V reads of k-step kk
+  // and dim tile dt: lane a of a 16-lane group points at key 16 kk + 4 kg + a / 4 (and
+  // +8), dims 32 dt + dsub .. +3, so that lane i of the group receives, as its element j,
+  // dim 32 dt + 16 ((lane / 16) % 2) + i of key 16 kk + 4 kg + j (and +8): the keys of the
+  // B operand's elements (the score accumulator layout).
+  const int a16 = lane & 15;
+  const int dsub = 16 * ((lane >> 4) & 1) + 4 * (a16 & 3);
+
   auto tile_compute = [&](auto b, int kb) {
     uint4 (*kt)[CH] = kbuf(b);
     uint4 (*vt)[CH] = vbuf(b);
-    // ---- S^T = K Q^T: two 32-key halves x two pair groups ----
-    floatx16 sacc[2][PG];
+
+    // ---- S^T = K Q^T: 2 KS MFMAs in (ks, key half) order, operand reads kAhead ahead ----
+    constexpr int NQK = 2 * KS;
+    constexpr int kAhead = 6;
+    auto kread = [&](auto mc) -> uint4 {
+      constexpr int m = decltype(mc)::value;
+      const int r = (m % 2) * 32 + n;
+      return kt[r][(2 * (m / 2) + kg) ^ chunk_swizzle<CH>(r)];
+    };
+    uint4 kop[NQK];
+    floatx16 sacc[2];
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-      for (int pg = 0; pg < PG; ++pg)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[kh][pg][i] = 0.f;
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const int r = kh * 32 + n;                 // key row this lane feeds as A
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 kv = kt[r][(ks * 2 + kg) ^ chunk_swizzle<CH>(r)];
-#pragma unroll
-        for (int pg = 0; pg < PG; ++pg)
-          sacc[kh][pg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kv), qreg[pg][ks],
-                                                                 sacc[kh][pg], 0, 0, 0);
-      }
-    }
+      for (int i = 0; i < 16; ++i) sacc[kh][i] = 0.f;
+    static_for<kAhead>([&](auto mc) { kop[decltype(mc)::value] = kread(mc); });
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<NQK>([&](auto mc) {
+      constexpr int m = decltype(mc)::value;
+      sacc[m % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kop[m]), qreg[m / 2],
+                                                            sacc[m % 2], 0, 0, 0);
+      if constexpr (m + kAhead < NQK) kop[m + kAhead] = kread(IntC<m + kAhead>());
+      __builtin_amdgcn_sched_barrier(0);
+    });
 
-    // ---- causal mask, tile max (exp2 domain: c times the raw maximum) ----
+    // ---- causal mask (tiles that cross a row's diagonal only), tile max ----
     // accumulator element i of half kh holds key kb + 32 kh + 8 (i / 4) + 4 kg + i % 4
-    const bool need_mask = kb + kKT - 1 > wave_lim_min;
-    float m_new[PG];
-    bool grow = false;
-#pragma unroll
-    for (int pg = 0; pg < PG; ++pg) {
-      float tmax = -INFINITY;
+    if (kb + kKT - 1 > wave_lim_min) {
+      const int rel = lim - kb - 4 * kg;         // elements at offsets above rel are masked
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float v = sacc[kh][pg][i];
-          if (need_mask) {
-            const int key = kb + kh * 32 + 8 * (i / 4) + 4 * kg + (i % 4);
-            if (key > lim[pg]) v = -INFINITY;
-          }
-          sacc[kh][pg][i] = v;
-          tmax = fmaxf(tmax, v);
-        }
+        for (int i = 0; i < 16; ++i)
+          if (32 * kh + 8 * (i / 4) + (i % 4) > rel) sacc[kh][i] = -INFINITY;
+    }
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sacc[kh][i]);
+    {
       const int x = __float_as_int(tmax);
       const auto sw = __builtin_amdgcn_permlane32_swap(x, x, false, false);
       tmax = fmaxf(__int_as_float(sw[0]), __int_as_float(sw[1]));
-      m_new[pg] = fmaxf(m_run[pg], tmax * c);   // a fully masked column keeps its max
-      grow |= m_new[pg] > m_run[pg] + kRescaleSlack;
     }
+    const float m_new = fmaxf(m_run, tmax * c);   // a fully masked column keeps its max
+
     // ---- lazy rescale: only when some row's max has grown past the slack ----
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleSlack) != 0) {
+      const float alpha = fast_exp2(m_run - m_new);   // 0 on the first tile
+      m_run = m_new;
+      l_part *= alpha;
 #pragma unroll
-      for (int pg = 0; pg < PG; ++pg) {
-        const float alpha = fast_exp2(m_run[pg] - m_new[pg]);   // 0 on the first tile
-        m_run[pg] = m_new[pg];
-        l_part[pg] *= alpha;
+      for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[pg][dt][i] *= alpha;
-      }
-    }
-    // ---- weights 2^(c s - m) (below 2^8), bf16 P^T operands, row sums of the bf16 weights ----
-    bf16x8 pb[PG][4];
-#pragma unroll
-    for (int pg = 0; pg < PG; ++pg) {
-      const float neg_m = -m_run[pg];
-      float psum = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          pb[pg][kk][j] = (__bf16)fast_exp2(fmaf(sacc[kk >> 1][pg][(kk & 1) * 8 + j], c, neg_m));   // 0 when masked
-        const uint4 pw = __builtin_bit_cast(uint4, pb[pg][kk]);
-        psum = dot2_bf16(pw.x, 0x3f803f80u, psum);   // + p0 + p1 (bf16 1.0 pairs)
-        psum = dot2_bf16(pw.y, 0x3f803f80u, psum);
-        psum = dot2_bf16(pw.z, 0x3f803f80u, psum);
-        psum = dot2_bf16(pw.w, 0x3f803f80u, psum);
-      }
-      l_part[pg] += psum;
+        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
     }
 
-    // ---- O^T += V^T P^T over four 16-key steps ----
-    // A operand of lane (dim 32 dt + n, k-group kg): keys 16 kk + 4 kg + 0..3 and +8..+11,
-    // the keys of the B operand's elements.  A transposing read gives lane i of a 16-lane
-    // group element i % 4 of the 8 bytes addressed by lane 4 j + i / 4 as its element j, so
-    // lane a of the group points at key t0 + a / 4, dims dbase + 4 (a % 4) .. +3.
-    const int a16 = lane & 15;
-    const int dsub = 16 * ((lane >> 4) & 1) + 4 * (a16 & 3);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    // ---- O^T += V^T P^T over four 16-key steps; the weights of step kk + 1 are
+    //      computed while the MFMAs of step kk run ----
+    const float neg_m = -m_run;
+    float psum = 0.f;
+    auto vread = [&](int kk, int dt) -> bf16x8 {
       const int t_lo = 16 * kk + 4 * kg + (a16 >> 2);
       const int t_hi = t_lo + 8;
+      const int dim = 32 * dt + dsub;
+      const int ch = dim / 8, half = (dim % 8) / 4;
+      const short* lo_p = reinterpret_cast<const short*>(&vt[t_lo][ch ^ chunk_swizzle<CH>(t_lo)]) + 4 * half;
+      const short* hi_p = reinterpret_cast<const short*>(&vt[t_hi][ch ^ chunk_swizzle<CH>(t_hi)]) + 4 * half;
+      const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)lo_p);
+      const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)hi_p);
+      const short8v av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      return __builtin_bit_cast(bf16x8, av);
+    };
+    // weights 2^(c s - m) of step kk (below 2^8) as the bf16 B operand; the row sum adds
+    // the same bf16 values (two per v_dot2_f32_bf16)
+    auto make_p = [&](auto kkc) -> bf16x8 {
+      constexpr int kk = decltype(kkc)::value;
+      bf16x8 pv;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int dim = 32 * dt + dsub;
-        const int ch = dim / 8, half = (dim % 8) / 4;
-        const short* lo_p = reinterpret_cast<const short*>(&vt[t_lo][ch ^ chunk_swizzle<CH>(t_lo)]) + 4 * half;
-        const short* hi_p = reinterpret_cast<const short*>(&vt[t_hi][ch ^ chunk_swizzle<CH>(t_hi)]) + 4 * half;
-        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)lo_p);
-        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)hi_p);
-        const short8v av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-        for (int pg = 0; pg < PG; ++pg)
-          oacc[pg][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pb[pg][kk],
-                                                                 oacc[pg][dt], 0, 0, 0);
-      }
-    }
+      for (int j = 0; j < 8; ++j)
+        pv[j] = (__bf16)fast_exp2(fmaf(sacc[kk >> 1][(kk & 1) * 8 + j], c, neg_m));   // 0 when masked
+      const uint4 pw = __builtin_bit_cast(uint4, pv);
+      psum = dot2_bf16(pw.x, 0x3f803f80u, psum);   // + p0 + p1 (a pair of bf16 ones)
+      psum = dot2_bf16(pw.y, 0x3f803f80u, psum);
+      psum = dot2_bf16(pw.z, 0x3f803f80u, psum);
+      psum = dot2_bf16(pw.w, 0x3f803f80u, psum);
+      return pv;
+    };
+    bf16x8 vop[2][DT];
+    bf16x8 pb[4];
+    static_for<DT>([&](auto dt) { vop[0][decltype(dt)::value] = vread(0, dt); });
+    pb[0] = make_p(IntC<0>());
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<4>([&](auto kkc) {
+      constexpr int kk = decltype(kkc)::value;
+      if constexpr (kk + 1 < 4)
+        static_for<DT>([&](auto dt) { vop[(kk + 1) % 2][decltype(dt)::value] = vread(kk + 1, dt); });
+      static_for<DT>([&](auto dtc) {
+        constexpr int dt = decltype(dtc)::value;
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[kk % 2][dt], pb[kk], oacc[dt], 0, 0, 0);
+      });
+      if constexpr (kk + 1 < 4) pb[kk + 1] = make_p(IntC<kk + 1>());
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    l_part += psum;
   };
 
   // ---- pipeline over tiles: tile t in buffer t % kBuf, the next kBuf - 1 tiles in flight ----
@@ -420,26 +416,23 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
   }
 
   // ---- finish: O / l, bf16 out; lane holds dims 32 dt + 8 q + 4 kg + 0..3 of its pair ----
+  const int x = __float_as_int(l_part);
+  const auto sw = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  const float l_tot = __int_as_float(sw[0]) + __int_as_float(sw[1]);
+  if (!pvalid) return;
+  const float inv = 1.f / l_tot;
+  uint16_t* op = p.out + ((size_t)(row0 + jrow) * Hq + (size_t)h * G + gq) * D;
 #pragma unroll
-  for (int pg = 0; pg < PG; ++pg) {
-    const int x = __float_as_int(l_part[pg]);
-    const auto sw = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    const float l_tot = __int_as_float(sw[0]) + __int_as_float(sw[1]);
-    if (!pvalid[pg]) continue;
-    const float inv = 1.f / l_tot;
-    uint16_t* op = p.out + ((size_t)(row0 + jrow[pg]) * Hq + (size_t)h * G + gq[pg]) * D;
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = dt * 32 + 8 * q4 + 4 * kg;
-        const uint32_t w0 = (uint32_t)f32_to_bf16_rne(oacc[pg][dt][q4 * 4 + 0] * inv) |
-                            ((uint32_t)f32_to_bf16_rne(oacc[pg][dt][q4 * 4 + 1] * inv) << 16);
-        const uint32_t w1 = (uint32_t)f32_to_bf16_rne(oacc[pg][dt][q4 * 4 + 2] * inv) |
-                            ((uint32_t)f32_to_bf16_rne(oacc[pg][dt][q4 * 4 + 3] * inv) << 16);
-        *reinterpret_cast<uint2*>(op + d) = make_uint2(w0, w1);
-      }
-  }
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = dt * 32 + 8 * q4 + 4 * kg;
+      const uint32_t w0 = (uint32_t)f32_to_bf16_rne(oacc[dt][q4 * 4 + 0] * inv) |
+                          ((uint32_t)f32_to_bf16_rne(oacc[dt][q4 * 4 + 1] * inv) << 16);
+      const uint32_t w1 = (uint32_t)f32_to_bf16_rne(oacc[dt][q4 * 4 + 2] * inv) |
+                          ((uint32_t)f32_to_bf16_rne(oacc[dt][q4 * 4 + 3] * inv) << 16);
+      *reinterpret_cast<uint2*>(op + d) = make_uint2(w0, w1);
+    }
 }
 
 template <int D>
