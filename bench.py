@@ -1,4 +1,4 @@
-"""Benchmark of one step of the paged attention path on one MI355X.
+"""Benchmark of the paged attention path on one MI355X.
 
 A step = kv_append of the batch's new tokens + one paged_attention call over
 the batch (every row of the hot path), on seeded synthetic inputs already
@@ -8,14 +8,23 @@ blocks).  Several device copies of the batch are cycled so consecutive steps
 do not re-read the same lines from the 256 MB last-level cache.
 
 Prints ONE JSON line on stdout:
-  value       KV-read GB/s of the whole step: algorithmic K+V bytes (every
-              cached token of every sequence read once) / step time;
-  roofline    the attention call (split-K decode + merge), timed with HIP
-              events on its stream around every call of the timed region,
-              against the 8 TB/s HBM peak; `traffic` comes from rocprofv3
-              FETCH_SIZE/WRITE_SIZE counters stored under profiles/ (null if
-              the kernels changed since);
-  cpu_baseline the float64 CPU oracle on a bounded sample of the same batch.
+  value         KV-read GB/s of the whole step: algorithmic K+V bytes (every
+                cached token of every sequence read once) / step time;
+  roofline      the attention call (split-K decode + merge), timed with HIP
+                events on its stream around every call of the timed region,
+                against the 8 TB/s HBM peak; `traffic` comes from rocprofv3
+                FETCH_SIZE/WRITE_SIZE counters stored under profiles/ (null if
+                the kernels changed since);
+  call_us       median / p10 / p90 of those per-call times, and the median
+                with the same copy re-read (hot last-level cache);
+  prefill       the other half of the metric: the chunked-prefill rows of the
+                mixed batch (8 chunks of 512 rows over prefixes of 0..2048
+                tokens, 32/8 heads, d 128) in a call of their own, TFLOP/s of
+                causal pairs against the 2.5 PFLOP/s bf16 peak;
+  mixed         (mixed batch only) decode-only and prefill-only sub-batch times;
+  append        kv_append alone at T = 64, 4288 and 65536 tokens (HBM GB/s);
+  measured_peaks a device copy and a bf16 GEMM through torch, for context;
+  cpu_baseline  the float64 CPU oracle on a bounded sample of the same batch.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config i]
 """
@@ -70,9 +79,13 @@ def traffic_from_profile(cfg: int, kernel_key: str):
     return ent.get("hbm_bytes_per_call")
 
 
+def pct(xs, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
+
+
 def cpu_baseline(wl, k2, v2, budget_s: float):
     """Time the float64 oracle (as it stands) on whole sequences of the batch until the budget is used."""
-    import numpy as np
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -105,6 +118,127 @@ def cpu_baseline(wl, k2, v2, budget_s: float):
                       f"BLAS threads {threads}, host cores {cores}"}
 
 
+class Device:
+    """Device-side copy of a workload (pools with this step's tokens not yet appended)."""
+
+    def __init__(self, wl, dev, torch):
+        import numpy as np
+        self.wl, self.dev, self.torch = wl, dev, torch
+
+        def up(a, dt):
+            if dt == torch.bfloat16:
+                return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        self.up = up
+        self.t = dict(q=up(wl.q, torch.bfloat16), k_new=up(wl.k_new, torch.bfloat16),
+                      v_new=up(wl.v_new, torch.bfloat16), slots=up(wl.slot_mapping, torch.int64),
+                      kc=up(wl.k_cache, torch.bfloat16), vc=up(wl.v_cache, torch.bfloat16),
+                      bt=up(wl.block_tables, torch.int32), sl=up(wl.seq_lens, torch.int32),
+                      qsl=up(wl.query_start_loc, torch.int32))
+
+    def clone(self):
+        c = object.__new__(Device)
+        c.wl, c.dev, c.torch, c.up = self.wl, self.dev, self.torch, self.up
+        c.t = {k: v.clone() for k, v in self.t.items()}
+        return c
+
+    def subset(self, seqs):
+        """Query rows, tables and lengths of the listed sequences (pools shared, already appended)."""
+        import numpy as np
+        torch, wl = self.torch, self.wl
+        seqs = np.asarray(seqs, dtype=np.int64)
+        qsl = wl.query_start_loc
+        rows = np.concatenate([np.arange(qsl[s], qsl[s + 1]) for s in seqs]) if len(seqs) else np.zeros(0, np.int64)
+        ql = (qsl[seqs + 1] - qsl[seqs]).astype(np.int32)
+        sub_qsl = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+        return dict(q=self.t["q"][torch.from_numpy(rows).to(self.dev)].contiguous(),
+                    bt=self.up(wl.block_tables[seqs], torch.int32), sl=self.up(wl.seq_lens[seqs], torch.int32),
+                    qsl=self.up(sub_qsl, torch.int32), num_seqs=len(seqs), max_query_len=int(ql.max()) if len(ql) else 0)
+
+
+def time_calls(fn, n, warm, stream, torch):
+    """HIP-event times (ms) of n calls of fn on `stream`, after `warm` untimed calls."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def sub_attention_ms(pkv, d, sub, scale, stream, torch, n=20):
+    """Per-call times of paged_attention over a sub-batch (its own output and workspace)."""
+    wl = d.wl
+    out = torch.empty_like(sub["q"])
+    ws = torch.empty(pkv.workspace_bytes(sub["num_seqs"], wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                         wl.max_blocks_per_seq, wl.block_size), dtype=torch.uint8, device=d.dev)
+
+    def call():
+        pkv.paged_attention(out, sub["q"], d.t["kc"], d.t["vc"], sub["bt"], sub["sl"], sub["qsl"], scale,
+                            sub["max_query_len"], workspace=ws, stream=stream)
+    return time_calls(call, n, 3, stream, torch)
+
+
+def prefill_report(pkv, d, stream, torch):
+    wl = d.wl
+    pre = wl.prefill_seqs()
+    flops = 4 * wl.head_dim * wl.num_q_heads * wl.causal_pairs(pre)
+    ms = sub_attention_ms(pkv, d, d.subset(pre), wl.scale, stream, torch)
+    med = pct(ms, 50)
+    tf = flops / (med * 1e-3) / 1e12
+    return {"workload": f"prefill rows of {wl.name}: {len(pre)} chunks, {int(wl.query_lens[pre].sum())} rows, "
+                        f"prefixes {sorted(int(wl.seq_lens[s] - wl.query_lens[s]) for s in pre)}",
+            "flops_per_call": flops, "call_us_median": round(med * 1e3, 3),
+            "call_us_p10": round(pct(ms, 10) * 1e3, 3), "call_us_p90": round(pct(ms, 90) * 1e3, 3),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                         "note": "flops = 4 d Hq x causal (row, key) pairs; the call also launches the "
+                                 "(empty) decode and merge grids and the planner"}}
+
+
+def append_report(pkv, dev, torch, stream):
+    """kv_append alone into a scratch pool: T new tokens of 8 KV heads x d 128 to random distinct slots."""
+    Hkv, D, bs = 8, 128, 16
+    res = {}
+    for T in (64, 4288, 65536):
+        nb = (T + bs - 1) // bs + 16
+        kc = torch.zeros(nb, bs, Hkv, D, dtype=torch.bfloat16, device=dev)
+        vc = torch.zeros_like(kc)
+        kn = torch.randn(T, Hkv, D, device=dev).to(torch.bfloat16)
+        vn = torch.randn(T, Hkv, D, device=dev).to(torch.bfloat16)
+        g = torch.Generator(device="cpu").manual_seed(T)
+        slots = torch.randperm(nb * bs, generator=g)[:T].to(torch.int64).to(dev)
+
+        def call():
+            pkv.kv_append(kn, vn, slots, kc, vc, stream=stream)
+        ms = time_calls(call, 20, 3, stream, torch)
+        med = pct(ms, 50)
+        moved = 2 * 2 * T * Hkv * D * 2     # K and V, read once and written once
+        res[f"T{T}"] = {"us_median": round(med * 1e3, 3), "GBps": round(moved / (med * 1e-3) / 1e9, 1)}
+        del kc, vc, kn, vn, slots
+    return res
+
+
+def measured_peaks(torch, dev, stream):
+    x = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+    x.fill_(1.0)
+    y = torch.empty_like(x)
+    ms = time_calls(lambda: y.copy_(x), 10, 2, stream, torch)
+    copy_gbs = 2 * x.numel() * 4 / (pct(ms, 50) * 1e-3) / 1e9
+    del x, y
+    n = 8192
+    a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    ms = time_calls(lambda: torch.mm(a, b), 10, 3, stream, torch)
+    tf = 2 * n ** 3 / (pct(ms, 50) * 1e-3) / 1e12
+    return {"device_copy_GBps": round(copy_gbs, 1), "device_copy_note": "1 GiB copy, bytes read + written",
+            "bf16_gemm_TFLOPs": round(tf, 1), "bf16_gemm_note": "torch.mm 8192^3 bf16 (hipBLASLt)"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,6 +248,8 @@ def main():
     ap.add_argument("--copies", type=int, default=3, help="device copies of the batch cycled per step")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the prefill, append and peak measurements (step timing and roofline only)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the step, run a plain device copy of MIB MiB --steps times "
                          "(reference kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -147,42 +283,38 @@ def main():
 
     log(f"generating config {args.config} ...")
     wl = workloads.make_config(args.config)
-
-    def up(a, dt):
-        if dt == torch.bfloat16:
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-
-    base = dict(q=up(wl.q, torch.bfloat16), k_new=up(wl.k_new, torch.bfloat16), v_new=up(wl.v_new, torch.bfloat16),
-                slots=up(wl.slot_mapping, torch.int64), kc=up(wl.k_cache, torch.bfloat16),
-                vc=up(wl.v_cache, torch.bfloat16), bt=up(wl.block_tables, torch.int32),
-                sl=up(wl.seq_lens, torch.int32), qsl=up(wl.query_start_loc, torch.int32))
-    copies = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(args.copies - 1)]
+    base = Device(wl, dev, torch)
+    copies = [base] + [base.clone() for _ in range(args.copies - 1)]
     ws_bytes = pkv.workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
                                    wl.max_blocks_per_seq, wl.block_size)
     for c in copies:
-        c["out"] = torch.empty_like(c["q"])
-        c["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        c.t["out"] = torch.empty_like(c.t["q"])
+        c.t["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(c, ev=None):
-        pkv.kv_append(c["k_new"], c["v_new"], c["slots"], c["kc"], c["vc"], stream=stream)
-        if ev is not None:
-            ev[0].record(stream)
-        pkv.paged_attention(c["out"], c["q"], c["kc"], c["vc"], c["bt"], c["sl"], c["qsl"], wl.scale,
-                            wl.max_query_len, workspace=c["ws"], stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
+    def append(c):
+        t = c.t
+        pkv.kv_append(t["k_new"], t["v_new"], t["slots"], t["kc"], t["vc"], stream=stream)
+
+    def attend(c):
+        t = c.t
+        pkv.paged_attention(t["out"], t["q"], t["kc"], t["vc"], t["bt"], t["sl"], t["qsl"], wl.scale,
+                            wl.max_query_len, workspace=t["ws"], stream=stream)
 
     for i in range(args.warmup):
-        step(copies[i % len(copies)])
+        append(copies[i % len(copies)])
+        attend(copies[i % len(copies)])
     torch.cuda.synchronize()
 
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(copies[i % len(copies)], evs[i])
+        c = copies[i % len(copies)]
+        append(c)
+        evs[i][0].record(stream)
+        attend(c)
+        evs[i][1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
@@ -193,9 +325,9 @@ def main():
     uniq_bytes = wl.unique_kv_read_bytes()
     dec = wl.decode_seqs()
     pre = wl.prefill_seqs()
-    flops = 4 * wl.head_dim * wl.num_q_heads * wl.causal_pairs(pre)
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = uniq_bytes / (attn_avg_ms * 1e-3) / 1e9
+    hot_ms = time_calls(lambda: attend(copies[0]), 10, 2, stream, torch)
 
     result = {
         "metric": METRIC,
@@ -221,12 +353,44 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "avg_call_us": round(attn_avg_ms * 1e3, 3),
                      "algorithmic_bytes_per_call": uniq_bytes,
                      "traffic": traffic_from_profile(args.config, "paged_attention")},
+        "call_us": {"median": round(pct(attn_ms, 50) * 1e3, 3), "p10": round(pct(attn_ms, 10) * 1e3, 3),
+                    "p90": round(pct(attn_ms, 90) * 1e3, 3),
+                    "hot_cache_median": round(pct(hot_ms, 50) * 1e3, 3)},
     }
-    if len(pre):
-        result["prefill_tflops_if_alone"] = None   # the mixed call is reported as one unit
-        result["prefill_flops_per_call"] = flops
     log(f"step {ms_per_step * 1e3:.1f} us, attention call {attn_avg_ms * 1e3:.1f} us, "
         f"{value:.0f} GB/s step, {achieved:.0f} GB/s attention")
+
+    if not args.no_extras:
+        if len(pre):
+            # the mixed batch itself: decode-only and prefill-only sub-batches
+            dms = sub_attention_ms(pkv, base, base.subset(dec), wl.scale, stream, torch)
+            dmed = pct(dms, 50)
+            ub = wl.unique_kv_read_bytes(dec)
+            result["mixed"] = {"decode_only_call_us_median": round(dmed * 1e3, 3),
+                               "decode_only_unique_GBps": round(ub / (dmed * 1e-3) / 1e9, 1),
+                               "decode_only_logical_GBps": round(wl.kv_read_bytes(dec) / (dmed * 1e-3) / 1e9, 1),
+                               "mixed_call_us_median": result["call_us"]["median"]}
+            result["prefill"] = prefill_report(pkv, base, stream, torch)
+            result["mixed"]["prefill_only_call_us_median"] = result["prefill"]["call_us_median"]
+            del copies
+        else:
+            del copies, base
+            torch.cuda.empty_cache()
+            log("generating the mixed batch for its prefill rows ...")
+            wl3 = workloads.make_config(3)
+            d3 = Device(wl3, dev, torch)
+            # the pools must hold this step's tokens before attention reads them
+            pkv.kv_append(d3.t["k_new"], d3.t["v_new"], d3.t["slots"], d3.t["kc"], d3.t["vc"], stream=stream)
+            result["prefill"] = prefill_report(pkv, d3, stream, torch)
+            del d3
+        torch.cuda.empty_cache()
+        result["append"] = append_report(pkv, dev, torch, stream)
+        result["measured_peaks"] = measured_peaks(torch, dev, stream)
+        result["measured_peaks"]["decode_frac_of_device_copy"] = round(
+            achieved / result["measured_peaks"]["device_copy_GBps"], 4)
+        if "prefill" in result:
+            result["measured_peaks"]["prefill_frac_of_bf16_gemm"] = round(
+                result["prefill"]["roofline"]["achieved"] / result["measured_peaks"]["bf16_gemm_TFLOPs"], 4)
 
     if not args.no_cpu:
         import oracle
