@@ -6,13 +6,15 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "kernels.h"
 #include "pagedkv.h"
 
 namespace {
 
-constexpr int kSplitTokens = 512;   // split-K size of decode rows (a multiple of 64)
+constexpr int kMinShareTokens = 512;   // smallest key range a decode wave takes (a multiple of 64)
+constexpr int kDecodeWavesPerCU = 8;   // resident decode waves per compute unit (2 per SIMD)
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -21,26 +23,47 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 struct WsLayout {
   int64_t max_splits;
   int64_t plan_capacity;
-  size_t o_off, m_off, l_off, count_off, items_off, total;
+  size_t o_off, m_off, l_off, nparts_off, count_off, items_off, total;
 };
 
-// Split-K partials of decode rows, then the prefill planner's count and work list.
-// Depends only on (num_seqs, Hq, Hkv, D, max_blocks, bs), so a caller can size it once.
+// Split-K partials of decode rows and their piece counts, then the prefill planner's
+// count and work list.  Depends only on (num_seqs, Hq, Hkv, D, max_blocks, bs), so a
+// caller can size it once.  A decode wave's share is at least kMinShareTokens keys, so
+// a (sequence, head) of at most max_blocks * bs keys is cut into at most
+// ceil(max_tokens / kMinShareTokens) + 1 pieces.
 WsLayout workspace_layout(int num_seqs, int Hq, int Hkv, int D, int max_blocks, int bs) {
   WsLayout w{};
   const int64_t max_tokens = (int64_t)max_blocks * bs;
-  w.max_splits = (max_tokens + kSplitTokens - 1) / kSplitTokens;
-  if (w.max_splits < 1) w.max_splits = 1;
+  w.max_splits = (max_tokens + kMinShareTokens - 1) / kMinShareTokens + 1;
   const int rows = pkv::kPrefillPairs / (Hq / Hkv);
   w.plan_capacity = (int64_t)num_seqs * ((max_tokens + rows - 1) / rows);
   const size_t cells = (size_t)num_seqs * Hq * w.max_splits;
   w.o_off = 0;
   w.m_off = round_up(cells * D * sizeof(float), 256);
   w.l_off = w.m_off + round_up(cells * sizeof(float), 256);
-  w.count_off = w.l_off + round_up(cells * sizeof(float), 256);
+  w.nparts_off = w.l_off + round_up(cells * sizeof(float), 256);
+  w.count_off = w.nparts_off + round_up((size_t)num_seqs * Hkv * sizeof(int), 256);
   w.items_off = w.count_off + 256;
   w.total = w.items_off + round_up((size_t)w.plan_capacity * 8, 256);
   return w;
+}
+
+// Decode waves of one call: the device's compute units times the resident waves per unit,
+// looked up once per device.
+int decode_waves_for_current_device() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = -1;
+  if (dev >= 0) {
+    const int v = cached[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0;
+  if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  const int waves = cus * kDecodeWavesPerCU;
+  if (dev >= 0) cached[dev].store(waves, std::memory_order_relaxed);
+  return waves;
 }
 
 }  // namespace
@@ -106,6 +129,9 @@ int paged_attention(void* out, const void* q, const void* k_cache, const void* v
   if (num_seqs > 65535 || num_q_heads > 65535) return PKV_EUNSUPPORTED;   // grid y/z limits
   const WsLayout ws = workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size);
   if (ws.max_splits > 65535 || ws.plan_capacity > INT32_MAX) return PKV_EUNSUPPORTED;
+  // decode work units (sequence, KV head, 64-token tile) are counted in 32 bits
+  if ((int64_t)num_seqs * num_kv_heads * (((int64_t)max_blocks_per_seq * block_size + 63) / 64) > INT32_MAX)
+    return PKV_EUNSUPPORTED;
   if (!workspace) {
     *workspace_bytes = ws.total;
     return PKV_OK;
@@ -137,12 +163,14 @@ int paged_attention(void* out, const void* q, const void* k_cache, const void* v
   p.D = head_dim;
   p.bs = block_size;
   p.scale_log2 = scale * 1.4426950408889634f;
-  p.split_tokens = kSplitTokens;
+  p.decode_waves = decode_waves_for_current_device();
+  p.min_share_tiles = kMinShareTokens / 64;
   p.max_splits = ws.max_splits;
   char* wsb = (char*)workspace;
   p.ws_o = (float*)(wsb + ws.o_off);
   p.ws_m = (float*)(wsb + ws.m_off);
   p.ws_l = (float*)(wsb + ws.l_off);
+  p.ws_nparts = (int*)(wsb + ws.nparts_off);
   p.plan_count = (int*)(wsb + ws.count_off);
   p.plan_items = (int2*)(wsb + ws.items_off);
   p.plan_capacity = (int)ws.plan_capacity;

@@ -52,9 +52,28 @@ typedef short short4v __attribute__((ext_vector_type(4)));
 typedef short short8v __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) short4v lds_short4;
 
+// Tiles (64 tokens) of decode sequence s, 0 for a sequence with no decode row.
+__device__ __forceinline__ int decode_tiles(const AttnParams& p, int s) {
+  const int row0 = p.qsl[s];
+  if (p.qsl[s + 1] - row0 != 1 || row0 < 0 || row0 >= p.num_q_tokens) return 0;
+  const int L = min(p.seq_lens[s], p.max_blocks * p.bs);   // clamp a length the table cannot map
+  return L > 0 ? (L + kTile - 1) / kTile : 0;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int d = 1; d < kWave; d *= 2) {
+    const int y = __shfl_up(v, d, kWave);
+    if (lane >= d) v += y;
+  }
+  return v;
+}
+
 template <int D, int G, int BS>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 8)))
-void decode_split_kernel(AttnParams p) {
+void decode_kernel(AttnParams p) {
   constexpr int CH = D / 8;              // 16-byte chunks per row
   constexpr int RPI = kWave / CH;        // rows per wave-wide load (4 at d 128)
   constexpr int NL = kTile / RPI;        // loads per lane per tile, for K and for V
@@ -67,204 +86,254 @@ void decode_split_kernel(AttnParams p) {
 
   __shared__ __attribute__((aligned(16))) uint4 tile[kTile][CH];   // K, then V, of the current tile
 
-  // KV heads vary fastest across workgroups: the heads of one split read the same pool
-  // rows (heads are interleaved in a slot), so they are dispatched together.
-  const int h = blockIdx.x, split = blockIdx.y, s = blockIdx.z;
-  const int row0 = p.qsl[s];
-  if (p.qsl[s + 1] - row0 != 1) return;          // not a decode row
-  if (row0 < 0 || row0 >= p.num_q_tokens) return;
-  const int L = min(p.seq_lens[s], p.max_blocks * BS);   // clamp a length the table cannot map
-  const int t_begin = split * p.split_tokens;
-  if (t_begin >= L) return;                      // split past the end of the sequence
-  const int t_end = min(t_begin + p.split_tokens, L);
-  const int nsplit = (L + p.split_tokens - 1) / p.split_tokens;
-
   const int lane = threadIdx.x;
+  const int w = blockIdx.x;
+  const int Hkv = p.Hkv;
+
+  // ---- the partition: units (s, h, tile) in that order, an equal share per wave ----
+  // Lane l sums the tiles of sequences [l c, (l + 1) c); a wave scan gives each lane the
+  // units before its chunk.  Unit counts fit in 32 bits (checked by the host).
+  const int c_per = (p.num_seqs + kWave - 1) / kWave;
+  int my_tiles = 0;
+  for (int i = 0; i < c_per; ++i) {
+    const int s = lane * c_per + i;
+    if (s < p.num_seqs) my_tiles += decode_tiles(p, s);
+  }
+  const int incl = wave_incl_scan(my_tiles);
+  const int total_units = uniform(__shfl(incl, kWave - 1, kWave) * Hkv);
+  if (total_units == 0) return;
+  const int share = uniform(max(p.min_share_tiles, (total_units + p.decode_waves - 1) / p.decode_waves));
+  if (w >= (total_units + share - 1) / share) return;   // fewer shares than waves
+  const int x0 = w * share;
+  const int x1 = min(x0 + share, total_units);
+  // the lane whose chunk holds unit x0, then the sequence inside that chunk
+  const int excl_units = (incl - my_tiles) * Hkv;
+  const unsigned long long hit = __builtin_amdgcn_ballot_w64(excl_units <= x0 && x0 < incl * Hkv);
+  const int src = (int)__builtin_ctzll(hit);     // nonempty: x0 < total_units
+  int s = uniform(src * c_per);
+  int seg_a = uniform(__shfl(excl_units, src, kWave));   // first unit of sequence s
+  int nt = uniform(decode_tiles(p, s));
+  while (x0 >= seg_a + Hkv * nt && s + 1 < p.num_seqs) {
+    seg_a += Hkv * nt;
+    s = uniform(s + 1);
+    nt = uniform(decode_tiles(p, s));
+  }
+
   const int n = lane & 15;                       // accumulator column: query head of the group
   const int kg = lane >> 4;                      // k-group / accumulator row group
-  const int Hq = p.Hkv * G;
-  const int* bt_row = p.block_tables + (size_t)s * p.max_blocks;
-  const size_t row_stride = (size_t)p.Hkv * D;   // elements per pool slot
-  const char* kbase = reinterpret_cast<const char*>(p.k_cache + (size_t)h * D);
-  const char* vbase = reinterpret_cast<const char*>(p.v_cache + (size_t)h * D);
+  const int Hq = Hkv * G;
+  const size_t row_stride = (size_t)Hkv * D;     // elements per pool slot
   const int nblocks = p.num_blocks > 0x7fffffff ? 0x7fffffff : (int)p.num_blocks;
   const size_t blk_bytes = (size_t)BS * row_stride * 2;
   const uint32_t row_bytes = (uint32_t)(row_stride * 2);
   const float c = p.scale_log2;
   const int lrow = lane / CH, lch = lane % CH;   // this lane's row (within a load) and chunk
-
-  // ---- Q^T as the B operand: head n, dims ks*32 + kg*8 .. +8 (zero for padding heads) ----
-  bf16x8 qreg[KS];
-  {
-    const uint16_t* qp = p.q + ((size_t)row0 * Hq + (size_t)h * G + (n < G ? n : 0)) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (n < G) v = *reinterpret_cast<const uint4*>(qp + ks * 32 + kg * 8);
-      qreg[ks] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-
-  floatx4 oacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_part = 0.f;
-
-  // Block-table entries of a tile (wave-uniform scalar loads).  Entries past the end,
-  // or outside the pool, become block 0: a safe address whose rows the masks ignore.
-  auto load_bts = [&](int t0, int* dst) {
-#pragma unroll
-    for (int j = 0; j < NBT; ++j) {
-      const int b = (t0 + j * BS < t_end) ? bt_row[uniform((t0 + j * BS) / BS)] : 0;
-      dst[j] = (unsigned)b < (unsigned)nblocks ? b : 0;
-    }
-  };
-  // Coalesced tile load: load i covers rows RPI*i .. RPI*i + RPI - 1 (one pool block).
   const uint32_t lane_off = (uint32_t)lrow * row_bytes + (uint32_t)lch * 16;
-  auto issue = [&](const char* base, const int* bb, uint4* reg) {
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const char* b = base + (size_t)bb[(RPI * i) / BS] * blk_bytes + (uint32_t)((RPI * i) % BS) * row_bytes;
-      reg[i] = load_stream16(b + lane_off);
-    }
-  };
-  // Registers -> LDS, row-major, chunk c of row r at c ^ (r % CH); rows >= nvalid get zeros.
-  auto stage = [&](const uint4* reg, int nvalid) {
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const int r = RPI * i + lrow;
-      uint4 v = reg[i];
-      if (nvalid < kTile && r >= nvalid) v = make_uint4(0u, 0u, 0u, 0u);
-      tile[r][lch ^ (r % CH)] = v;
-    }
-  };
 
-  const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
-  int bts[NBT];
-  load_bts(t_begin, bts);
-  uint4 kreg[NL], vreg[NL];
-  issue(kbase, bts, kreg);
-  issue(vbase, bts, vreg);
-  for (int tile_i = 0; tile_i < ntiles; ++tile_i) {
-    const int ts = t_begin + tile_i * kTile;
-    const int nvalid = min(kTile, t_end - ts);
-    const bool has_next = tile_i + 1 < ntiles;
-    int bts_next[NBT];
-#pragma unroll
-    for (int j = 0; j < NBT; ++j) bts_next[j] = 0;
-    if (has_next) load_bts(ts + kTile, bts_next);
+  // One piece: tiles [tb0, tb1) of (sequence s, KV head h), whose units start at unit a.
+  auto piece = [&](int h, int tb0, int tb1, int a) {
+    const int row0 = uniform(p.qsl[s]);
+    const int L = uniform(min(p.seq_lens[s], p.max_blocks * BS));
+    const int t_begin = tb0 * kTile;
+    const int t_end = min(tb1 * kTile, L);
+    const int* bt_row = p.block_tables + (size_t)s * p.max_blocks;
+    const char* kbase = reinterpret_cast<const char*>(p.k_cache + (size_t)h * D);
+    const char* vbase = reinterpret_cast<const char*>(p.v_cache + (size_t)h * D);
 
-    // ---- K tile -> LDS; refill the K registers with the next tile ----
-    stage(kreg, nvalid);
-    __builtin_amdgcn_sched_barrier(0);
-    if (has_next) issue(kbase, bts_next, kreg);
-    wave_lds_sync();
-
-    // ---- S^T = K Q^T ----
-    floatx4 sacc[TB];
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-      sacc[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
-      const int r = tb * 16 + n;
+    // ---- Q^T as the B operand: head n, dims ks*32 + kg*8 .. +8 (zero for padding heads) ----
+    bf16x8 qreg[KS];
+    {
+      const uint16_t* qp = p.q + ((size_t)row0 * Hq + (size_t)h * G + (n < G ? n : 0)) * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const uint4 kv = tile[r][(ks * 4 + kg) ^ (r % CH)];
-        sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qreg[ks], sacc[tb], 0, 0, 0);
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (n < G) v = *reinterpret_cast<const uint4*>(qp + ks * 32 + kg * 8);
+        qreg[ks] = __builtin_bit_cast(bf16x8, v);
       }
     }
-    wave_lds_sync();                             // K reads done before V overwrites the buffer
 
-    // ---- V tile -> LDS; refill the V registers with the next tile ----
-    stage(vreg, nvalid);
-    __builtin_amdgcn_sched_barrier(0);
-    if (has_next) issue(vbase, bts_next, vreg);
+    floatx4 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_part = 0.f;
 
-    // ---- online softmax for head n over this tile's tokens (exp2 domain) ----
-    float tmax = -INFINITY;
+    // Block-table entries of a tile (wave-uniform scalar loads).  Entries past the end,
+    // or outside the pool, become block 0: a safe address whose rows the masks ignore.
+    auto load_bts = [&](int t0, int* dst) {
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = tb * 16 + 4 * kg + i;      // token of this accumulator element
-        const float v = (r < nvalid) ? sacc[tb][i] * c : -INFINITY;
-        sacc[tb][i] = v;
-        tmax = fmaxf(tmax, v);
+      for (int j = 0; j < NBT; ++j) {
+        const int b = (t0 + j * BS < t_end) ? bt_row[uniform((t0 + j * BS) / BS)] : 0;
+        dst[j] = (unsigned)b < (unsigned)nblocks ? b : 0;
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-    const float mn = fmaxf(m_run, tmax);         // finite: token 0 of the tile is valid
-    const float alpha = fast_exp2(m_run - mn);   // 0 on the first tile
-    m_run = mn;
-    float psum = 0.f;
+    };
+    // Coalesced tile load: load i covers rows RPI*i .. RPI*i + RPI - 1 (one pool block).
+    auto issue = [&](const char* base, const int* bb, uint4* reg) {
 #pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = fast_exp2(sacc[tb][i] - mn);   // 0 for masked tokens
-        sacc[tb][i] = e;
-        psum += e;
+      for (int i = 0; i < NL; ++i) {
+        const char* b = base + (size_t)bb[(RPI * i) / BS] * blk_bytes + (uint32_t)((RPI * i) % BS) * row_bytes;
+        reg[i] = load_stream16(b + lane_off);
       }
-    l_part = l_part * alpha + psum;
+    };
+    // Registers -> LDS, row-major, chunk c of row r at c ^ (r % CH); rows >= nvalid get zeros.
+    auto stage = [&](const uint4* reg, int nvalid) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) oacc[db][i] *= alpha;
-    wave_lds_sync();                             // V is in LDS
+      for (int i = 0; i < NL; ++i) {
+        const int r = RPI * i + lrow;
+        uint4 v = reg[i];
+        if (nvalid < kTile && r >= nvalid) v = make_uint4(0u, 0u, 0u, 0u);
+        tile[r][lch ^ (r % CH)] = v;
+      }
+    };
 
-    // ---- O^T += V^T P^T, two 32-token k-steps ----
-    // The A operand of lane (dim n, k-group kg) holds tokens t_lo + 0..3 and t_lo + 16..19
-    // (t_lo = 32 kk + 4 kg), matching the score accumulator layout of the B operand.  A
-    // transposing read returns, in lane i of a 16-lane group, element i % 4 of the 8 bytes
-    // addressed by lane 4 j + i / 4 as its element j: lane a of the group therefore points
-    // at token t_lo + a / 4, dims d0 + 4 (a % 4) .. +3.
+    const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
+    int bts[NBT];
+    load_bts(t_begin, bts);
+    uint4 kreg[NL], vreg[NL];
+    issue(kbase, bts, kreg);
+    issue(vbase, bts, vreg);
+    for (int tile_i = 0; tile_i < ntiles; ++tile_i) {
+      const int ts = t_begin + tile_i * kTile;
+      const int nvalid = min(kTile, t_end - ts);
+      const bool has_next = tile_i + 1 < ntiles;
+      int bts_next[NBT];
 #pragma unroll
-    for (int kk = 0; kk < TB / 2; ++kk) {
-      bf16x8 pb;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pb[i] = (__bf16)sacc[2 * kk][i];
-        pb[4 + i] = (__bf16)sacc[2 * kk + 1][i];
-      }
-      const int tr = 32 * kk + 4 * kg + n / 4;   // token row this lane addresses
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int dim = db * 16 + 4 * (n % 4);   // first of the 4 dims this lane addresses
-        const int ch = dim / 8, half = (dim % 8) / 4;
-        const short* lo_p = reinterpret_cast<const short*>(&tile[tr][ch ^ (tr % CH)]) + 4 * half;
-        const short* hi_p = reinterpret_cast<const short*>(&tile[tr + 16][ch ^ ((tr + 16) % CH)]) + 4 * half;
-        const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)lo_p);
-        const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)hi_p);
-        const short8v av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pb, oacc[db], 0, 0, 0);
-      }
-    }
-    wave_lds_sync();                             // V reads done before the next K lands
-#pragma unroll
-    for (int j = 0; j < NBT; ++j) bts[j] = bts_next[j];
-  }
+      for (int j = 0; j < NBT; ++j) bts_next[j] = 0;
+      if (has_next) load_bts(ts + kTile, bts_next);
 
-  // ---- finish: lane (kg, n) holds dims db*16 + 4kg + i of head n ----
-  float l_tot = l_part + __shfl_xor(l_part, 16, kWave);
-  l_tot += __shfl_xor(l_tot, 32, kWave);
-  if (n < G) {
-    const int qh = h * G + n;
-    if (nsplit == 1) {
-      const float inv = 1.f / l_tot;
-      uint16_t* op = p.out + ((size_t)row0 * Hq + qh) * D;
+      // ---- K tile -> LDS; refill the K registers with the next tile ----
+      stage(kreg, nvalid);
+      __builtin_amdgcn_sched_barrier(0);
+      if (has_next) issue(kbase, bts_next, kreg);
+      wave_lds_sync();
+
+      // ---- S^T = K Q^T ----
+      floatx4 sacc[TB];
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const uint32_t w0 = (uint32_t)f32_to_bf16_rne(oacc[db][0] * inv) | ((uint32_t)f32_to_bf16_rne(oacc[db][1] * inv) << 16);
-        const uint32_t w1 = (uint32_t)f32_to_bf16_rne(oacc[db][2] * inv) | ((uint32_t)f32_to_bf16_rne(oacc[db][3] * inv) << 16);
-        *reinterpret_cast<uint2*>(op + db * 16 + 4 * kg) = make_uint2(w0, w1);
+      for (int tb = 0; tb < TB; ++tb) {
+        sacc[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        const int r = tb * 16 + n;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint4 kv = tile[r][(ks * 4 + kg) ^ (r % CH)];
+          sacc[tb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qreg[ks], sacc[tb], 0, 0, 0);
+        }
       }
-    } else {
-      const size_t idx = ((size_t)s * Hq + qh) * p.max_splits + split;
+      wave_lds_sync();                           // K reads done before V overwrites the buffer
+
+      // ---- V tile -> LDS; refill the V registers with the next tile ----
+      stage(vreg, nvalid);
+      __builtin_amdgcn_sched_barrier(0);
+      if (has_next) issue(vbase, bts_next, vreg);
+
+      // ---- online softmax for head n over this tile's tokens (exp2 domain) ----
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = tb * 16 + 4 * kg + i;    // token of this accumulator element
+          const float v = (r < nvalid) ? sacc[tb][i] * c : -INFINITY;
+          sacc[tb][i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+      const float mn = fmaxf(m_run, tmax);       // finite: token 0 of the tile is valid
+      const float alpha = fast_exp2(m_run - mn); // 0 on the first tile
+      m_run = mn;
+      float psum = 0.f;
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = fast_exp2(sacc[tb][i] - mn);   // 0 for masked tokens
+          sacc[tb][i] = e;
+          psum += e;
+        }
+      l_part = l_part * alpha + psum;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        *reinterpret_cast<float4*>(p.ws_o + idx * D + db * 16 + 4 * kg) =
-            make_float4(oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]);
-      if (kg == 0) { p.ws_m[idx] = m_run; p.ws_l[idx] = l_tot; }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[db][i] *= alpha;
+      wave_lds_sync();                           // V is in LDS
+
+      // ---- O^T += V^T P^T, two 32-token k-steps ----
+      // The A operand of lane (dim n, k-group kg) holds tokens t_lo + 0..3 and t_lo + 16..19
+      // (t_lo = 32 kk + 4 kg), matching the score accumulator layout of the B operand.  A
+      // transposing read returns, in lane i of a 16-lane group, element i % 4 of the 8 bytes
+      // addressed by lane 4 j + i / 4 as its element j: lane a of the group therefore points
+      // at token t_lo + a / 4, dims d0 + 4 (a % 4) .. +3.
+#pragma unroll
+      for (int kk = 0; kk < TB / 2; ++kk) {
+        bf16x8 pb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pb[i] = (__bf16)sacc[2 * kk][i];
+          pb[4 + i] = (__bf16)sacc[2 * kk + 1][i];
+        }
+        const int tr = 32 * kk + 4 * kg + n / 4; // token row this lane addresses
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const int dim = db * 16 + 4 * (n % 4); // first of the 4 dims this lane addresses
+          const int ch = dim / 8, half = (dim % 8) / 4;
+          const short* lo_p = reinterpret_cast<const short*>(&tile[tr][ch ^ (tr % CH)]) + 4 * half;
+          const short* hi_p = reinterpret_cast<const short*>(&tile[tr + 16][ch ^ ((tr + 16) % CH)]) + 4 * half;
+          const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)lo_p);
+          const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)hi_p);
+          const short8v av = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pb, oacc[db], 0, 0, 0);
+        }
+      }
+      wave_lds_sync();                           // V reads done before the next K lands
+#pragma unroll
+      for (int j = 0; j < NBT; ++j) bts[j] = bts_next[j];
     }
+
+    // ---- finish: lane (kg, n) holds dims db*16 + 4kg + i of head n ----
+    const int first_w = a / share;                 // the wave holding tile 0 of (s, h)
+    const int nseg = (a + nt - 1) / share - first_w + 1;   // pieces of (s, h)
+    if (tb0 == 0 && lane == 0) p.ws_nparts[(size_t)s * Hkv + h] = nseg;
+    float l_tot = l_part + __shfl_xor(l_part, 16, kWave);
+    l_tot += __shfl_xor(l_tot, 32, kWave);
+    if (n < G) {
+      const int qh = h * G + n;
+      if (nseg == 1) {                           // the whole (s, h): final output
+        const float inv = 1.f / l_tot;
+        uint16_t* op = p.out + ((size_t)row0 * Hq + qh) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const uint32_t w0 = (uint32_t)f32_to_bf16_rne(oacc[db][0] * inv) | ((uint32_t)f32_to_bf16_rne(oacc[db][1] * inv) << 16);
+          const uint32_t w1 = (uint32_t)f32_to_bf16_rne(oacc[db][2] * inv) | ((uint32_t)f32_to_bf16_rne(oacc[db][3] * inv) << 16);
+          *reinterpret_cast<uint2*>(op + db * 16 + 4 * kg) = make_uint2(w0, w1);
+        }
+      } else {                                   // partial j = this wave's index among the pieces
+        const int j = w - first_w;
+        const size_t idx = ((size_t)s * Hq + qh) * p.max_splits + j;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+          *reinterpret_cast<float4*>(p.ws_o + idx * D + db * 16 + 4 * kg) =
+              make_float4(oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]);
+        if (kg == 0) { p.ws_m[idx] = m_run; p.ws_l[idx] = l_tot; }
+      }
+    }
+  };
+
+  // ---- walk the share: pieces of consecutive (s, h) segments ----
+  int pos = x0;
+  while (pos < x1) {
+    if (pos >= seg_a + Hkv * nt) {               // past sequence s: next sequence with decode tiles
+      if (s + 1 >= p.num_seqs) break;            // not reached: pos < total_units
+      seg_a += Hkv * nt;
+      s = uniform(s + 1);
+      nt = uniform(decode_tiles(p, s));
+      continue;
+    }
+    const int h = (pos - seg_a) / nt;
+    const int a = seg_a + h * nt;                // first unit of (s, h)
+    const int tb0 = pos - a;
+    const int tb1 = min(x1, a + nt) - a;
+    piece(h, tb0, tb1, a);
+    pos = a + tb1;
   }
 }
 
@@ -284,12 +353,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
   __shared__ float lpart[SL];
 
   const int qh = blockIdx.x, s = blockIdx.y;
+  if (decode_tiles(p, s) == 0) return;           // not a decode row (or nothing to attend)
   const int row0 = p.qsl[s];
-  if (p.qsl[s + 1] - row0 != 1) return;
-  if (row0 < 0 || row0 >= p.num_q_tokens) return;
-  const int L = min(p.seq_lens[s], p.max_blocks * p.bs);
-  const int nsplit = (L + p.split_tokens - 1) / p.split_tokens;
-  if (nsplit <= 1) return;                       // written directly by the split kernel
+  const int nsplit = p.ws_nparts[(size_t)s * p.Hkv + qh / (p.Hq / p.Hkv)];
+  if (nsplit <= 1) return;                       // written directly by the decode kernel
   const size_t base = ((size_t)s * p.Hq + qh) * p.max_splits;
   const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
 
@@ -334,8 +401,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
 
 template <int D, int G, int BS>
 hipError_t launch_decode_t(const AttnParams& p, hipStream_t stream) {
-  dim3 grid(p.Hkv, p.max_splits, p.num_seqs);
-  hipLaunchKernelGGL((decode_split_kernel<D, G, BS>), grid, dim3(kWave), 0, stream, p);
+  hipLaunchKernelGGL((decode_kernel<D, G, BS>), dim3(p.decode_waves), dim3(kWave), 0, stream, p);
   return hipGetLastError();
 }
 
