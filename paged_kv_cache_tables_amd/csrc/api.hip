@@ -126,7 +126,7 @@ int paged_attention(void* out, const void* q, const void* k_cache, const void* v
   const int G = num_q_heads / num_kv_heads;
   if (!pkv::decode_supported(head_dim, G, block_size) || !pkv::prefill_supported(head_dim, G, block_size))
     return PKV_EUNSUPPORTED;
-  if (num_seqs > 65535 || num_q_heads > 65535) return PKV_EUNSUPPORTED;   // grid y/z limits
+  if (num_seqs > 65535 || num_q_heads > 65535) return PKV_EUNSUPPORTED;   // 16-bit sequence and head counts
   const WsLayout ws = workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size);
   if (ws.max_splits > 65535 || ws.plan_capacity > INT32_MAX) return PKV_EUNSUPPORTED;
   // decode work units (sequence, KV head, 64-token tile) are counted in 32 bits

@@ -337,65 +337,71 @@ void decode_kernel(AttnParams p) {
   }
 }
 
-// Log-sum-exp merge of the splits of one (decode sequence, query head):
+// Log-sum-exp merge of the pieces of one (decode sequence, query head):
 // out = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j with M = max_j m_j.
-// 256 threads: thread t owns 4 dims (one float4 of every partial) and every
-// SL-th split, so SL partial rows are in flight at once; the SL partial sums
-// are then added through LDS.
-constexpr int kMergeThreads = 256;
+// A piece row of D floats is D / 4 lanes of float4, so a wave reads 64 / (D / 4) pieces
+// at once and adds its lane groups with lane exchanges.  Narrow form: one wave per
+// (sequence, query head), four per workgroup, for calls whose segments have few pieces.
+// Wide form: the four waves of a workgroup share one (sequence, query head) and are
+// combined through LDS, for long sequences cut into many pieces.
+constexpr int kMergeWaves = 4;
 
-template <int D>
-__global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
-  constexpr int LPD = D / 4;                     // threads per partial row
-  constexpr int SL = kMergeThreads / LPD;        // split lanes
-  __shared__ float4 part[SL][LPD];
-  __shared__ float red[kMergeThreads / kWave];
-  __shared__ float lpart[SL];
-
-  const int qh = blockIdx.x, s = blockIdx.y;
+template <int D, bool WIDE>
+__global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(AttnParams p) {
+  constexpr int LPP = D / 4;                     // lanes per piece row
+  constexpr int PPI = kWave / LPP;               // pieces per wave-wide step
+  constexpr int WPC = WIDE ? kMergeWaves : 1;    // waves per (sequence, query head)
+  __shared__ float4 part[WIDE ? kMergeWaves : 1][LPP];
+  __shared__ float lpart[WIDE ? kMergeWaves : 1];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = (int)(threadIdx.x / kWave);
+  const int cell = WIDE ? (int)blockIdx.x : (int)blockIdx.x * kMergeWaves + wv;   // (s, qh)
+  if (cell >= p.num_seqs * p.Hq) return;         // uniform over the workgroup in the wide form
+  const int s = cell / p.Hq, qh = cell % p.Hq;
   if (decode_tiles(p, s) == 0) return;           // not a decode row (or nothing to attend)
-  const int row0 = p.qsl[s];
   const int nsplit = p.ws_nparts[(size_t)s * p.Hkv + qh / (p.Hq / p.Hkv)];
   if (nsplit <= 1) return;                       // written directly by the decode kernel
+  const int row0 = p.qsl[s];
   const size_t base = ((size_t)s * p.Hq + qh) * p.max_splits;
-  const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
 
-  // M = max_j m_j
-  float M = -INFINITY;
-  for (int j = t; j < nsplit; j += kMergeThreads) M = fmaxf(M, p.ws_m[base + j]);
+  float M = -INFINITY;                           // every wave of the cell finds the same M
+  for (int j = lane; j < nsplit; j += kWave) M = fmaxf(M, p.ws_m[base + j]);
   M = wave_max(M);
-  if (lane == 0) red[w] = M;
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kMergeThreads / kWave; ++i) M = fmaxf(M, red[i]);
 
-  const int sl = t / LPD, dq = t % LPD;
+  const int sub = lane / LPP, dq = lane % LPP;
+  const int w_in = WIDE ? wv : 0;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float ls = 0.f;
 #pragma unroll 4
-  for (int j = sl; j < nsplit; j += SL) {
+  for (int j = w_in * PPI + sub; j < nsplit; j += WPC * PPI) {
     const float f = fast_exp2(p.ws_m[base + j] - M);
     const float4 o = *reinterpret_cast<const float4*>(p.ws_o + (base + j) * D + 4 * dq);
     acc.x = fmaf(f, o.x, acc.x); acc.y = fmaf(f, o.y, acc.y);
     acc.z = fmaf(f, o.z, acc.z); acc.w = fmaf(f, o.w, acc.w);
     ls = fmaf(f, p.ws_l[base + j], ls);
   }
-  part[sl][dq] = acc;
-  if (dq == 0) lpart[sl] = ls;
-  __syncthreads();
-  if (t < LPD) {
-    float4 o = part[0][t];
-    float l = lpart[0];
 #pragma unroll
-    for (int i = 1; i < SL; ++i) {
-      const float4 q4 = part[i][t];
-      o.x += q4.x; o.y += q4.y; o.z += q4.z; o.w += q4.w;
-      l += lpart[i];
+  for (int off = LPP; off < kWave; off *= 2) {
+    acc.x += __shfl_xor(acc.x, off, kWave); acc.y += __shfl_xor(acc.y, off, kWave);
+    acc.z += __shfl_xor(acc.z, off, kWave); acc.w += __shfl_xor(acc.w, off, kWave);
+    ls += __shfl_xor(ls, off, kWave);
+  }
+  if constexpr (WIDE) {
+    if (sub == 0) part[wv][dq] = acc;
+    if (lane == 0) lpart[wv] = ls;
+    __syncthreads();
+    if (wv != 0) return;
+    for (int i = 1; i < kMergeWaves; ++i) {
+      const float4 q4 = part[i][dq];
+      acc.x += q4.x; acc.y += q4.y; acc.z += q4.z; acc.w += q4.w;
+      ls += lpart[i];
     }
-    const float inv = 1.f / l;
-    const uint32_t w0 = (uint32_t)f32_to_bf16_rne(o.x * inv) | ((uint32_t)f32_to_bf16_rne(o.y * inv) << 16);
-    const uint32_t w1 = (uint32_t)f32_to_bf16_rne(o.z * inv) | ((uint32_t)f32_to_bf16_rne(o.w * inv) << 16);
-    *reinterpret_cast<uint2*>(p.out + ((size_t)row0 * p.Hq + qh) * D + 4 * t) = make_uint2(w0, w1);
+  }
+  if (sub == 0) {
+    const float inv = 1.f / ls;
+    const uint32_t w0 = (uint32_t)f32_to_bf16_rne(acc.x * inv) | ((uint32_t)f32_to_bf16_rne(acc.y * inv) << 16);
+    const uint32_t w1 = (uint32_t)f32_to_bf16_rne(acc.z * inv) | ((uint32_t)f32_to_bf16_rne(acc.w * inv) << 16);
+    *reinterpret_cast<uint2*>(p.out + ((size_t)row0 * p.Hq + qh) * D + 4 * dq) = make_uint2(w0, w1);
   }
 }
 
@@ -441,10 +447,21 @@ hipError_t launch_decode(const AttnParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_merge(const AttnParams& p, hipStream_t stream) {
-  dim3 grid(p.Hq, p.num_seqs);
-  if (p.D == 128) hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kMergeThreads), 0, stream, p);
-  else if (p.D == 64) hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kMergeThreads), 0, stream, p);
-  else return hipErrorInvalidValue;
+  // many pieces per (sequence, head) are possible only for long sequences: share a cell
+  // among the waves of a workgroup there
+  const int64_t cells = (int64_t)p.num_seqs * p.Hq;
+  const bool wide = p.max_splits > 32;
+  const dim3 grid((unsigned)(wide ? cells : (cells + kMergeWaves - 1) / kMergeWaves));
+  const dim3 block(kMergeWaves * kWave);
+  if (p.D == 128) {
+    if (wide) hipLaunchKernelGGL((merge_kernel<128, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((merge_kernel<128, false>), grid, block, 0, stream, p);
+  } else if (p.D == 64) {
+    if (wide) hipLaunchKernelGGL((merge_kernel<64, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((merge_kernel<64, false>), grid, block, 0, stream, p);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
