@@ -52,13 +52,19 @@ typedef short short4v __attribute__((ext_vector_type(4)));
 typedef short short8v __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) short4v lds_short4;
 
-// Tiles (64 tokens) of decode sequence s, 0 for a sequence with no decode row.
-__device__ __forceinline__ int decode_tiles(const AttnParams& p, int s) {
+// Query row, key count and 64-token tiles of decode sequence s (no tiles for a
+// sequence with no decode row).
+struct SeqInfo {
+  int row0, len, tiles;
+};
+__device__ __forceinline__ SeqInfo seq_info(const AttnParams& p, int s) {
   const int row0 = p.qsl[s];
-  if (p.qsl[s + 1] - row0 != 1 || row0 < 0 || row0 >= p.num_q_tokens) return 0;
-  const int L = min(p.seq_lens[s], p.max_blocks * p.bs);   // clamp a length the table cannot map
-  return L > 0 ? (L + kTile - 1) / kTile : 0;
+  const int q = p.qsl[s + 1] - row0;
+  const int len = min(p.seq_lens[s], p.max_blocks * p.bs);   // clamp a length the table cannot map
+  if (q != 1 || row0 < 0 || row0 >= p.num_q_tokens || len <= 0) return SeqInfo{row0, 0, 0};
+  return SeqInfo{row0, len, (len + kTile - 1) / kTile};
 }
+__device__ __forceinline__ int decode_tiles(const AttnParams& p, int s) { return seq_info(p, s).tiles; }
 
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {
@@ -95,9 +101,14 @@ void decode_kernel(AttnParams p) {
   // units before its chunk.  Unit counts fit in 32 bits (checked by the host).
   const int c_per = (p.num_seqs + kWave - 1) / kWave;
   int my_tiles = 0;
+  SeqInfo first{0, 0, 0};                        // this lane's first sequence
   for (int i = 0; i < c_per; ++i) {
     const int s = lane * c_per + i;
-    if (s < p.num_seqs) my_tiles += decode_tiles(p, s);
+    if (s < p.num_seqs) {
+      const SeqInfo si = seq_info(p, s);
+      if (i == 0) first = si;
+      my_tiles += si.tiles;
+    }
   }
   const int incl = wave_incl_scan(my_tiles);
   const int total_units = uniform(__shfl(incl, kWave - 1, kWave) * Hkv);
@@ -112,12 +123,18 @@ void decode_kernel(AttnParams p) {
   const int src = (int)__builtin_ctzll(hit);     // nonempty: x0 < total_units
   int s = uniform(src * c_per);
   int seg_a = uniform(__shfl(excl_units, src, kWave));   // first unit of sequence s
-  int nt = uniform(decode_tiles(p, s));
-  while (x0 >= seg_a + Hkv * nt && s + 1 < p.num_seqs) {
+  int cur_row0 = uniform(__shfl(first.row0, src, kWave));
+  int cur_len = uniform(__shfl(first.len, src, kWave));
+  int nt = uniform(__shfl(first.tiles, src, kWave));
+  auto next_seq = [&]() {
     seg_a += Hkv * nt;
     s = uniform(s + 1);
-    nt = uniform(decode_tiles(p, s));
-  }
+    const SeqInfo si = seq_info(p, s);
+    cur_row0 = uniform(si.row0);
+    cur_len = uniform(si.len);
+    nt = uniform(si.tiles);
+  };
+  while (x0 >= seg_a + Hkv * nt && s + 1 < p.num_seqs) next_seq();
 
   const int n = lane & 15;                       // accumulator column: query head of the group
   const int kg = lane >> 4;                      // k-group / accumulator row group
@@ -132,8 +149,8 @@ void decode_kernel(AttnParams p) {
 
   // One piece: tiles [tb0, tb1) of (sequence s, KV head h), whose units start at unit a.
   auto piece = [&](int h, int tb0, int tb1, int a) {
-    const int row0 = uniform(p.qsl[s]);
-    const int L = uniform(min(p.seq_lens[s], p.max_blocks * BS));
+    const int row0 = cur_row0;
+    const int L = cur_len;
     const int t_begin = tb0 * kTile;
     const int t_end = min(tb1 * kTile, L);
     const int* bt_row = p.block_tables + (size_t)s * p.max_blocks;
@@ -323,9 +340,7 @@ void decode_kernel(AttnParams p) {
   while (pos < x1) {
     if (pos >= seg_a + Hkv * nt) {               // past sequence s: next sequence with decode tiles
       if (s + 1 >= p.num_seqs) break;            // not reached: pos < total_units
-      seg_a += Hkv * nt;
-      s = uniform(s + 1);
-      nt = uniform(decode_tiles(p, s));
+      next_seq();
       continue;
     }
     const int h = (pos - seg_a) / nt;
