@@ -144,6 +144,14 @@ EDGE = [
      8, 2, 128, 16),
     ("long-single", [(20000, 1)], 32, 8, 128, 16),
     ("chunk-from-zero", [(512, 512), (97, 97)], 32, 8, 128, 16),
+    # decode work is cut into equal shares of (sequence, KV head, 64-token tile) units:
+    # many short sequences (a lane scans several, a share spans many segments) ...
+    ("many-short-decode", [(1 + (i * 37) % 130, 1) for i in range(300)], 8, 2, 128, 16),
+    # ... decode rows around prefill rows that the partition skips ...
+    ("decode-around-prefill", [(41 + (i * 211) % 900, 1 if i % 7 else 40) for i in range(90)], 16, 4, 128, 16),
+    # ... and long sequences cut into ~200 pieces (the merge's wide form), d 128 and d 64
+    ("long-many-pieces", [(100000, 1)], 8, 2, 128, 16),
+    ("long-d64-wide-merge", [(40000, 1), (3, 1)], 8, 2, 64, 16),
 ]
 
 
