@@ -175,7 +175,8 @@ def sub_attention_ms(pkv, d, sub, scale, stream, torch, n=20):
     wl = d.wl
     out = torch.empty_like(sub["q"])
     ws = torch.empty(pkv.workspace_bytes(sub["num_seqs"], wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
-                                         wl.max_blocks_per_seq, wl.block_size), dtype=torch.uint8, device=d.dev)
+                                         wl.max_blocks_per_seq, wl.block_size, max(1, sub["max_query_len"])),
+                     dtype=torch.uint8, device=d.dev)
 
     def call():
         pkv.paged_attention(out, sub["q"], d.t["kc"], d.t["vc"], sub["bt"], sub["sl"], sub["qsl"], scale,
@@ -286,7 +287,7 @@ def main():
     base = Device(wl, dev, torch)
     copies = [base] + [base.clone() for _ in range(args.copies - 1)]
     ws_bytes = pkv.workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
-                                   wl.max_blocks_per_seq, wl.block_size)
+                                   wl.max_blocks_per_seq, wl.block_size, wl.max_query_len)
     for c in copies:
         c.t["out"] = torch.empty_like(c.t["q"])
         c.t["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)

@@ -131,8 +131,11 @@ PKV_API int kv_append(const void* k_new, const void* v_new, const int64_t* slot_
  * block block_tables[s, t / block_size], offset t % block_size
  * ([TGI] "Under the Hood: PagedAttention" / "Under the Hood: Flash
  * Attention": exact softmax attention, never materialising the score matrix).
- * Decode rows use split-K with a log-sum-exp merge; prefill rows use bf16
- * matrix-core products with fp32 accumulation.  out is rounded to bf16
+ * Rows of sequences with q_s <= 16 / (num_q_heads / num_kv_heads) -- decode
+ * rows and short chunks such as speculative-decoding verification -- share one
+ * K/V read per sequence and KV head through split-K with a log-sum-exp merge;
+ * longer chunks (chunked prefill) use tiled bf16 matrix-core products.  Both
+ * accumulate in fp32.  out is rounded to bf16
  * (nearest-even).  Positions >= L and unreferenced blocks are never read into
  * the result (they may hold any bits, NaN included).
  *
@@ -147,7 +150,8 @@ PKV_API int kv_append(const void* k_new, const void* v_new, const int64_t* slot_
  *   num_seqs, num_q_tokens   >= 0 (0 enqueues nothing).
  *   max_blocks_per_seq  row length of block_tables; also bounds L:
  *                  every L <= max_blocks_per_seq * block_size.
- *   max_query_len  >= every q_s (host-side bound; sizes the prefill grid).
+ *   max_query_len  >= every q_s (host-side bound; sizes the prefill grid and
+ *                  the decode-row partials of the workspace).
  *   num_q_heads, num_kv_heads   Hq % Hkv == 0 and Hq/Hkv in {1,2,4,8,16}.
  *   head_dim       64 or 128.
  *   num_blocks, block_size   pool shape; block_size in {8, 16, 32}.
@@ -158,7 +162,9 @@ PKV_API int kv_append(const void* k_new, const void* v_new, const int64_t* slot_
  *                  Otherwise *workspace_bytes is the size of the buffer the
  *                  caller passes (PKV_EWORKSPACE if smaller than required).
  *                  The size depends only on num_seqs, num_q_heads,
- *                  num_kv_heads, head_dim, max_blocks_per_seq and block_size.  The buffer needs no
+ *                  num_kv_heads, head_dim, max_blocks_per_seq, block_size
+ *                  and max_query_len (through min(max_query_len,
+ *                  16 / (num_q_heads / num_kv_heads))).  The buffer needs no
  *                  initialisation and must not be shared by calls that can
  *                  run concurrently.
  *   stream         hipStream_t.

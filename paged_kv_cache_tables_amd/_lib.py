@@ -107,11 +107,12 @@ def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None
 
 
 def workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
-                    max_blocks_per_seq: int, block_size: int, num_blocks: int = 1) -> int:
+                    max_blocks_per_seq: int, block_size: int, max_query_len: int = 1,
+                    num_blocks: int = 1) -> int:
     """Size of the split-K workspace paged_attention needs (query mode of the C call)."""
     n = ctypes.c_size_t(0)
     st = load_library().paged_attention(None, None, None, None, None, None, None, num_seqs, 0,
-                                        max_blocks_per_seq, 0, num_q_heads, num_kv_heads, head_dim,
+                                        max_blocks_per_seq, max_query_len, num_q_heads, num_kv_heads, head_dim,
                                         num_blocks, block_size, 1.0, None, ctypes.byref(n), None)
     if st != 0:
         raise PagedKVError("paged_attention(workspace query)", st)

@@ -26,18 +26,25 @@ struct WsLayout {
   size_t o_off, m_off, l_off, nparts_off, count_off, items_off, total;
 };
 
+// Rows per sequence that are computed as decode rows: q_s x G (row, head) columns fill
+// at most the 16 columns of the decode kernel's score product.
+int decode_rows(int Hq, int Hkv, int max_query_len) {
+  const int by_columns = 16 / (Hq / Hkv);
+  return std::max(1, std::min(by_columns, max_query_len));
+}
+
 // Split-K partials of decode rows and their piece counts, then the prefill planner's
-// count and work list.  Depends only on (num_seqs, Hq, Hkv, D, max_blocks, bs), so a
-// caller can size it once.  A decode wave's share is at least kMinShareTokens keys, so
-// a (sequence, head) of at most max_blocks * bs keys is cut into at most
-// ceil(max_tokens / kMinShareTokens) + 1 pieces.
-WsLayout workspace_layout(int num_seqs, int Hq, int Hkv, int D, int max_blocks, int bs) {
+// count and work list.  Depends only on (num_seqs, Hq, Hkv, D, max_blocks, bs,
+// max_query_len), so a caller can size it once.  A decode wave's share is at least
+// kMinShareTokens keys, so a (sequence, head) of at most max_blocks * bs keys is cut
+// into at most ceil(max_tokens / kMinShareTokens) + 1 pieces.
+WsLayout workspace_layout(int num_seqs, int Hq, int Hkv, int D, int max_blocks, int bs, int max_query_len) {
   WsLayout w{};
   const int64_t max_tokens = (int64_t)max_blocks * bs;
   w.max_splits = (max_tokens + kMinShareTokens - 1) / kMinShareTokens + 1;
   const int rows = pkv::kPrefillPairs / (Hq / Hkv);
   w.plan_capacity = (int64_t)num_seqs * ((max_tokens + rows - 1) / rows);
-  const size_t cells = (size_t)num_seqs * Hq * w.max_splits;
+  const size_t cells = (size_t)num_seqs * decode_rows(Hq, Hkv, max_query_len) * Hq * w.max_splits;
   w.o_off = 0;
   w.m_off = round_up(cells * D * sizeof(float), 256);
   w.l_off = w.m_off + round_up(cells * sizeof(float), 256);
@@ -127,7 +134,8 @@ int paged_attention(void* out, const void* q, const void* k_cache, const void* v
   if (!pkv::decode_supported(head_dim, G, block_size) || !pkv::prefill_supported(head_dim, G, block_size))
     return PKV_EUNSUPPORTED;
   if (num_seqs > 65535 || num_q_heads > 65535) return PKV_EUNSUPPORTED;   // 16-bit sequence and head counts
-  const WsLayout ws = workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size);
+  const WsLayout ws = workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                                       block_size, max_query_len);
   if (ws.max_splits > 65535 || ws.plan_capacity > INT32_MAX) return PKV_EUNSUPPORTED;
   // decode work units (sequence, KV head, 64-token tile) are counted in 32 bits
   if ((int64_t)num_seqs * num_kv_heads * (((int64_t)max_blocks_per_seq * block_size + 63) / 64) > INT32_MAX)
@@ -164,6 +172,7 @@ int paged_attention(void* out, const void* q, const void* k_cache, const void* v
   p.bs = block_size;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.decode_waves = decode_waves_for_current_device();
+  p.decode_max_q = decode_rows(num_q_heads, num_kv_heads, max_query_len);
   p.min_share_tiles = kMinShareTokens / 64;
   p.max_splits = ws.max_splits;
   char* wsb = (char*)workspace;
@@ -185,7 +194,7 @@ int paged_attention(void* out, const void* q, const void* k_cache, const void* v
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = pkv::launch_decode(p, st);
   if (e == hipSuccess) e = pkv::launch_merge(p, st);
-  if (e == hipSuccess && max_query_len > 1) e = pkv::launch_prefill(p, st);
+  if (e == hipSuccess && max_query_len > p.decode_max_q) e = pkv::launch_prefill(p, st);
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 

@@ -52,17 +52,19 @@ typedef short short4v __attribute__((ext_vector_type(4)));
 typedef short short8v __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) short4v lds_short4;
 
-// Query row, key count and 64-token tiles of decode sequence s (no tiles for a
-// sequence with no decode row).
+// First query row, row count, key count and 64-token tiles of sequence s when its rows
+// are decode rows -- 1 <= q_s <= decode_max_q, so that its q_s x G (row, head) columns fit
+// the 16 columns of the score product -- and no tiles otherwise.
 struct SeqInfo {
-  int row0, len, tiles;
+  int row0, q, len, tiles;
 };
 __device__ __forceinline__ SeqInfo seq_info(const AttnParams& p, int s) {
   const int row0 = p.qsl[s];
   const int q = p.qsl[s + 1] - row0;
   const int len = min(p.seq_lens[s], p.max_blocks * p.bs);   // clamp a length the table cannot map
-  if (q != 1 || row0 < 0 || row0 >= p.num_q_tokens || len <= 0) return SeqInfo{row0, 0, 0};
-  return SeqInfo{row0, len, (len + kTile - 1) / kTile};
+  if (q < 1 || q > p.decode_max_q || row0 < 0 || row0 + q > p.num_q_tokens || len <= 0)
+    return SeqInfo{row0, 0, 0, 0};
+  return SeqInfo{row0, q, len, (len + kTile - 1) / kTile};
 }
 __device__ __forceinline__ int decode_tiles(const AttnParams& p, int s) { return seq_info(p, s).tiles; }
 
@@ -77,7 +79,9 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-template <int D, int G, int BS>
+// MULTI: some sequence may have several decode rows (decode_max_q > 1); otherwise every
+// column's causal limit is the sequence's last key and only the tile end masks.
+template <int D, int G, int BS, bool MULTI>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void decode_kernel(AttnParams p) {
   constexpr int CH = D / 8;              // 16-byte chunks per row
@@ -101,7 +105,7 @@ void decode_kernel(AttnParams p) {
   // units before its chunk.  Unit counts fit in 32 bits (checked by the host).
   const int c_per = (p.num_seqs + kWave - 1) / kWave;
   int my_tiles = 0;
-  SeqInfo first{0, 0, 0};                        // this lane's first sequence
+  SeqInfo first{0, 0, 0, 0};                     // this lane's first sequence
   for (int i = 0; i < c_per; ++i) {
     const int s = lane * c_per + i;
     if (s < p.num_seqs) {
@@ -124,6 +128,7 @@ void decode_kernel(AttnParams p) {
   int s = uniform(src * c_per);
   int seg_a = uniform(__shfl(excl_units, src, kWave));   // first unit of sequence s
   int cur_row0 = uniform(__shfl(first.row0, src, kWave));
+  int cur_q = uniform(__shfl(first.q, src, kWave));
   int cur_len = uniform(__shfl(first.len, src, kWave));
   int nt = uniform(__shfl(first.tiles, src, kWave));
   auto next_seq = [&]() {
@@ -131,6 +136,7 @@ void decode_kernel(AttnParams p) {
     s = uniform(s + 1);
     const SeqInfo si = seq_info(p, s);
     cur_row0 = uniform(si.row0);
+    cur_q = uniform(si.q);
     cur_len = uniform(si.len);
     nt = uniform(si.tiles);
   };
@@ -151,20 +157,25 @@ void decode_kernel(AttnParams p) {
   auto piece = [&](int h, int tb0, int tb1, int a) {
     const int row0 = cur_row0;
     const int L = cur_len;
+    // accumulator column n = (row rr of the sequence's q_s rows, head g of the group); the
+    // row at position L - q_s + rr attends keys 0..lim
+    const int rr = n / G, g = n % G;
+    const bool col_valid = rr < cur_q;
+    const int lim = col_valid ? L - cur_q + rr : L - 1;
     const int t_begin = tb0 * kTile;
     const int t_end = min(tb1 * kTile, L);
     const int* bt_row = p.block_tables + (size_t)s * p.max_blocks;
     const char* kbase = reinterpret_cast<const char*>(p.k_cache + (size_t)h * D);
     const char* vbase = reinterpret_cast<const char*>(p.v_cache + (size_t)h * D);
 
-    // ---- Q^T as the B operand: head n, dims ks*32 + kg*8 .. +8 (zero for padding heads) ----
+    // ---- Q^T as the B operand: column n, dims ks*32 + kg*8 .. +8 (zero for padding columns) ----
     bf16x8 qreg[KS];
     {
-      const uint16_t* qp = p.q + ((size_t)row0 * Hq + (size_t)h * G + (n < G ? n : 0)) * D;
+      const uint16_t* qp = p.q + ((size_t)(row0 + (col_valid ? rr : 0)) * Hq + (size_t)h * G + g) * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (n < G) v = *reinterpret_cast<const uint4*>(qp + ks * 32 + kg * 8);
+        if (col_valid) v = *reinterpret_cast<const uint4*>(qp + ks * 32 + kg * 8);
         qreg[ks] = __builtin_bit_cast(bf16x8, v);
       }
     }
@@ -242,28 +253,31 @@ void decode_kernel(AttnParams p) {
       __builtin_amdgcn_sched_barrier(0);
       if (has_next) issue(vbase, bts_next, vreg);
 
-      // ---- online softmax for head n over this tile's tokens (exp2 domain) ----
+      // ---- online softmax for column n over this tile's tokens (exp2 domain) ----
+      const int last = MULTI ? min(nvalid - 1, lim - ts) : nvalid - 1;   // last token column n sees
       float tmax = -INFINITY;
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = tb * 16 + 4 * kg + i;    // token of this accumulator element
-          const float v = (r < nvalid) ? sacc[tb][i] * c : -INFINITY;
+          const float v = (r <= last) ? sacc[tb][i] * c : -INFINITY;
           sacc[tb][i] = v;
           tmax = fmaxf(tmax, v);
         }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-      const float mn = fmaxf(m_run, tmax);       // finite: token 0 of the tile is valid
-      const float alpha = fast_exp2(m_run - mn); // 0 on the first tile
+      const float mn = fmaxf(m_run, tmax);       // -inf while column n has seen no key of this piece
+      // a column that has seen no key of this piece (only with several rows) keeps weights 0
+      const float m_use = (MULTI && mn == -INFINITY) ? 0.f : mn;
+      const float alpha = fast_exp2(m_run - m_use);   // 0 until the column's first visible key
       m_run = mn;
       float psum = 0.f;
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float e = fast_exp2(sacc[tb][i] - mn);   // 0 for masked tokens
+          const float e = fast_exp2(sacc[tb][i] - m_use);   // 0 for masked tokens
           sacc[tb][i] = e;
           psum += e;
         }
@@ -306,31 +320,35 @@ void decode_kernel(AttnParams p) {
       for (int j = 0; j < NBT; ++j) bts[j] = bts_next[j];
     }
 
-    // ---- finish: lane (kg, n) holds dims db*16 + 4kg + i of head n ----
+    // ---- finish: lane (kg, n) holds dims db*16 + 4kg + i of column n ----
+    // (the column's row and head are recomputed here rather than kept live through the loop)
+    int n_e = n, kg_e = kg;
+    asm volatile("" : "+v"(n_e), "+v"(kg_e));
+    const int rr_e = n_e / G, g_e = n_e % G;
     const int first_w = a / share;                 // the wave holding tile 0 of (s, h)
     const int nseg = (a + nt - 1) / share - first_w + 1;   // pieces of (s, h)
     if (tb0 == 0 && lane == 0) p.ws_nparts[(size_t)s * Hkv + h] = nseg;
     float l_tot = l_part + __shfl_xor(l_part, 16, kWave);
     l_tot += __shfl_xor(l_tot, 32, kWave);
-    if (n < G) {
-      const int qh = h * G + n;
+    if (rr_e < cur_q) {
+      const int qh = h * G + g_e;
       if (nseg == 1) {                           // the whole (s, h): final output
         const float inv = 1.f / l_tot;
-        uint16_t* op = p.out + ((size_t)row0 * Hq + qh) * D;
+        uint16_t* op = p.out + ((size_t)(row0 + rr_e) * Hq + qh) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const uint32_t w0 = (uint32_t)f32_to_bf16_rne(oacc[db][0] * inv) | ((uint32_t)f32_to_bf16_rne(oacc[db][1] * inv) << 16);
           const uint32_t w1 = (uint32_t)f32_to_bf16_rne(oacc[db][2] * inv) | ((uint32_t)f32_to_bf16_rne(oacc[db][3] * inv) << 16);
-          *reinterpret_cast<uint2*>(op + db * 16 + 4 * kg) = make_uint2(w0, w1);
+          *reinterpret_cast<uint2*>(op + db * 16 + 4 * kg_e) = make_uint2(w0, w1);
         }
       } else {                                   // partial j = this wave's index among the pieces
         const int j = w - first_w;
-        const size_t idx = ((size_t)s * Hq + qh) * p.max_splits + j;
+        const size_t idx = (((size_t)s * p.decode_max_q + rr_e) * Hq + qh) * p.max_splits + j;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
-          *reinterpret_cast<float4*>(p.ws_o + idx * D + db * 16 + 4 * kg) =
+          *reinterpret_cast<float4*>(p.ws_o + idx * D + db * 16 + 4 * kg_e) =
               make_float4(oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]);
-        if (kg == 0) { p.ws_m[idx] = m_run; p.ws_l[idx] = l_tot; }
+        if (kg_e == 0) { p.ws_m[idx] = m_run; p.ws_l[idx] = l_tot; }
       }
     }
   };
@@ -370,59 +388,65 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(AttnParams p
   __shared__ float lpart[WIDE ? kMergeWaves : 1];
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = (int)(threadIdx.x / kWave);
-  const int cell = WIDE ? (int)blockIdx.x : (int)blockIdx.x * kMergeWaves + wv;   // (s, qh)
+  // cell = (sequence s, query head qh); its decode rows are merged one after the other
+  const int cell = WIDE ? (int)blockIdx.x : (int)blockIdx.x * kMergeWaves + wv;
   if (cell >= p.num_seqs * p.Hq) return;         // uniform over the workgroup in the wide form
   const int s = cell / p.Hq, qh = cell % p.Hq;
-  if (decode_tiles(p, s) == 0) return;           // not a decode row (or nothing to attend)
+  const SeqInfo si = seq_info(p, s);
+  if (si.tiles == 0) return;                     // no decode rows (or nothing to attend)
   const int nsplit = p.ws_nparts[(size_t)s * p.Hkv + qh / (p.Hq / p.Hkv)];
   if (nsplit <= 1) return;                       // written directly by the decode kernel
-  const int row0 = p.qsl[s];
-  const size_t base = ((size_t)s * p.Hq + qh) * p.max_splits;
-
-  float M = -INFINITY;                           // every wave of the cell finds the same M
-  for (int j = lane; j < nsplit; j += kWave) M = fmaxf(M, p.ws_m[base + j]);
-  M = wave_max(M);
-
   const int sub = lane / LPP, dq = lane % LPP;
   const int w_in = WIDE ? wv : 0;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float ls = 0.f;
+
+  for (int rr = 0; rr < si.q; ++rr) {
+    const size_t base = (((size_t)s * p.decode_max_q + rr) * p.Hq + qh) * p.max_splits;
+    float M = -INFINITY;                         // every wave of the cell finds the same M
+    for (int j = lane; j < nsplit; j += kWave) M = fmaxf(M, p.ws_m[base + j]);
+    M = wave_max(M);
+
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float ls = 0.f;
 #pragma unroll 4
-  for (int j = w_in * PPI + sub; j < nsplit; j += WPC * PPI) {
-    const float f = fast_exp2(p.ws_m[base + j] - M);
-    const float4 o = *reinterpret_cast<const float4*>(p.ws_o + (base + j) * D + 4 * dq);
-    acc.x = fmaf(f, o.x, acc.x); acc.y = fmaf(f, o.y, acc.y);
-    acc.z = fmaf(f, o.z, acc.z); acc.w = fmaf(f, o.w, acc.w);
-    ls = fmaf(f, p.ws_l[base + j], ls);
-  }
-#pragma unroll
-  for (int off = LPP; off < kWave; off *= 2) {
-    acc.x += __shfl_xor(acc.x, off, kWave); acc.y += __shfl_xor(acc.y, off, kWave);
-    acc.z += __shfl_xor(acc.z, off, kWave); acc.w += __shfl_xor(acc.w, off, kWave);
-    ls += __shfl_xor(ls, off, kWave);
-  }
-  if constexpr (WIDE) {
-    if (sub == 0) part[wv][dq] = acc;
-    if (lane == 0) lpart[wv] = ls;
-    __syncthreads();
-    if (wv != 0) return;
-    for (int i = 1; i < kMergeWaves; ++i) {
-      const float4 q4 = part[i][dq];
-      acc.x += q4.x; acc.y += q4.y; acc.z += q4.z; acc.w += q4.w;
-      ls += lpart[i];
+    for (int j = w_in * PPI + sub; j < nsplit; j += WPC * PPI) {
+      const float f = fast_exp2(p.ws_m[base + j] - M);   // 0 for a piece that saw no key of this row
+      const float4 o = *reinterpret_cast<const float4*>(p.ws_o + (base + j) * D + 4 * dq);
+      acc.x = fmaf(f, o.x, acc.x); acc.y = fmaf(f, o.y, acc.y);
+      acc.z = fmaf(f, o.z, acc.z); acc.w = fmaf(f, o.w, acc.w);
+      ls = fmaf(f, p.ws_l[base + j], ls);
     }
-  }
-  if (sub == 0) {
-    const float inv = 1.f / ls;
-    const uint32_t w0 = (uint32_t)f32_to_bf16_rne(acc.x * inv) | ((uint32_t)f32_to_bf16_rne(acc.y * inv) << 16);
-    const uint32_t w1 = (uint32_t)f32_to_bf16_rne(acc.z * inv) | ((uint32_t)f32_to_bf16_rne(acc.w * inv) << 16);
-    *reinterpret_cast<uint2*>(p.out + ((size_t)row0 * p.Hq + qh) * D + 4 * dq) = make_uint2(w0, w1);
+#pragma unroll
+    for (int off = LPP; off < kWave; off *= 2) {
+      acc.x += __shfl_xor(acc.x, off, kWave); acc.y += __shfl_xor(acc.y, off, kWave);
+      acc.z += __shfl_xor(acc.z, off, kWave); acc.w += __shfl_xor(acc.w, off, kWave);
+      ls += __shfl_xor(ls, off, kWave);
+    }
+    if constexpr (WIDE) {
+      if (sub == 0) part[wv][dq] = acc;
+      if (lane == 0) lpart[wv] = ls;
+      __syncthreads();
+      for (int i = 1; i < kMergeWaves; ++i) {
+        const float4 q4 = part[i][dq];
+        acc.x += q4.x; acc.y += q4.y; acc.z += q4.z; acc.w += q4.w;
+        ls += lpart[i];
+      }
+      __syncthreads();                           // LDS free for the next row
+    }
+    if (sub == 0 && w_in == 0) {
+      const float inv = 1.f / ls;
+      const uint32_t w0 = (uint32_t)f32_to_bf16_rne(acc.x * inv) | ((uint32_t)f32_to_bf16_rne(acc.y * inv) << 16);
+      const uint32_t w1 = (uint32_t)f32_to_bf16_rne(acc.z * inv) | ((uint32_t)f32_to_bf16_rne(acc.w * inv) << 16);
+      *reinterpret_cast<uint2*>(p.out + ((size_t)(si.row0 + rr) * p.Hq + qh) * D + 4 * dq) = make_uint2(w0, w1);
+    }
   }
 }
 
 template <int D, int G, int BS>
 hipError_t launch_decode_t(const AttnParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_kernel<D, G, BS>), dim3(p.decode_waves), dim3(kWave), 0, stream, p);
+  if (p.decode_max_q > 1)
+    hipLaunchKernelGGL((decode_kernel<D, G, BS, true>), dim3(p.decode_waves), dim3(kWave), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_kernel<D, G, BS, false>), dim3(p.decode_waves), dim3(kWave), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -23,11 +23,12 @@ struct AttnParams {
   int Hq, Hkv, D, bs;
   float scale_log2;               // softmax scale * log2(e): scores live in the exp2 domain
   int decode_waves;               // decode grid: one wave per resident wave slot of the device
+  int decode_max_q;               // sequences with 1 <= q_s <= this are decode rows (q_s x G <= 16)
   int min_share_tiles;            // smallest share of 64-token tiles a decode wave takes
   int max_splits;                 // pieces one (sequence, head) can be cut into: bounds the partials
-  float* ws_o;                    // [num_seqs, Hq, max_splits, D]  unnormalised partial outputs
-  float* ws_m;                    // [num_seqs, Hq, max_splits]     partial max (exp2 domain)
-  float* ws_l;                    // [num_seqs, Hq, max_splits]     partial sum of exponentials
+  float* ws_o;                    // [num_seqs, decode_max_q, Hq, max_splits, D]  unnormalised partials
+  float* ws_m;                    // [num_seqs, decode_max_q, Hq, max_splits]     partial max (exp2 domain)
+  float* ws_l;                    // [num_seqs, decode_max_q, Hq, max_splits]     partial sum of exponentials
   int* ws_nparts;                 // [num_seqs, Hkv]                pieces of each decode (sequence, head)
   int2* plan_items;               // prefill work list (sequence, row tile), written by the planner
   int* plan_count;                // number of valid items

@@ -66,11 +66,13 @@ typedef __attribute__((address_space(3))) short4v lds_short4;
 typedef __attribute__((address_space(3))) void lds_void;
 
 // Lists the prefill work items (sequence, row tile) of one call: a sequence
-// with q_s > 1 rows has ceil(q_s / rows_per_tile) row tiles, emitted last tile
-// first.  One block; sequences are scanned in chunks of the block size.
+// with q_s > min_rows rows (fewer are computed as decode rows) has
+// ceil(q_s / rows_per_tile) row tiles, emitted last tile first.  One block;
+// sequences are scanned in chunks of the block size.
 constexpr int kPlanThreads = 1024;
 
 __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(const int32_t* __restrict__ qsl, int num_seqs,
+                                                                    int min_rows,
                                                                     int rows_per_tile, int2* __restrict__ items,
                                                                     int* __restrict__ count, int capacity) {
   __shared__ int wave_tot[kPlanThreads / kWave];
@@ -83,7 +85,7 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(const int32_
     int nt = 0;
     if (s < num_seqs) {
       const int q = qsl[s + 1] - qsl[s];
-      if (q > 1) nt = (q + rows_per_tile - 1) / rows_per_tile;
+      if (q > min_rows) nt = (q + rows_per_tile - 1) / rows_per_tile;
     }
     // inclusive scan inside the wave, then across waves
     int incl = nt;
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
   const int s = it.x, mt = it.y;
   const int row0 = p.qsl[s];
   const int qn = p.qsl[s + 1] - row0;
-  if (qn <= 1) return;                           // decode rows are handled elsewhere
+  if (qn <= p.decode_max_q) return;              // decode rows are handled elsewhere
   const int j0 = mt * ROWS;
   if (j0 >= qn) return;
   if (row0 < 0 || row0 + qn > p.num_q_tokens) return;
@@ -439,7 +441,7 @@ template <int D>
 hipError_t dispatch_g(const AttnParams& p, hipStream_t stream) {
   const int G = p.Hq / p.Hkv;
   const int rows = kPairsPerBlock / G;
-  hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p.qsl, p.num_seqs, rows,
+  hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p.qsl, p.num_seqs, p.decode_max_q, rows,
                      p.plan_items, p.plan_count, p.plan_capacity);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -467,7 +469,7 @@ bool prefill_supported(int D, int G, int bs) {
 }
 
 hipError_t launch_prefill(const AttnParams& p, hipStream_t stream) {
-  if (p.max_query_len <= 1) return hipSuccess;
+  if (p.max_query_len <= p.decode_max_q) return hipSuccess;   // decode rows only
   if (p.D == 128) return dispatch_g<128>(p, stream);
   if (p.D == 64) return dispatch_g<64>(p, stream);
   return hipErrorInvalidValue;

@@ -94,7 +94,11 @@ def test_workspace_query_and_size(lib):
     assert n.value >= 4 * 4 * 1 * 66 * 4
     small = ctypes.c_size_t(n.value - 1)
     assert lib.paged_attention(*attn_args(workspace=FAKE, workspace_bytes=ctypes.byref(small))) == PKV_EWORKSPACE
-    assert pkv.workspace_bytes(4, 4, 2, 64, 4, 16) == n.value
+    assert pkv.workspace_bytes(4, 4, 2, 64, 4, 16, max_query_len=5) == n.value
+    # decode-row partials: one row slot per sequence at max_query_len 1, up to 16 / G
+    assert pkv.workspace_bytes(4, 4, 2, 64, 4, 16, max_query_len=1) < n.value
+    assert pkv.workspace_bytes(4, 4, 2, 64, 4, 16, max_query_len=500) == \
+        pkv.workspace_bytes(4, 4, 2, 64, 4, 16, max_query_len=8)
 
 
 @pytest.mark.parametrize("over,expect", [

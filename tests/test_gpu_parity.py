@@ -152,6 +152,14 @@ EDGE = [
     # ... and long sequences cut into ~200 pieces (the merge's wide form), d 128 and d 64
     ("long-many-pieces", [(100000, 1)], 8, 2, 128, 16),
     ("long-d64-wide-merge", [(40000, 1), (3, 1)], 8, 2, 64, 16),
+    # short chunks (q_s x G <= 16, e.g. speculative verification) run with the decode rows:
+    # every row its own causal limit, pieces and merge per (sequence, row, head)
+    ("multi-row-g4", [(700, 4), (5, 2), (1300, 3), (64, 4), (2, 2), (900, 1)], 16, 4, 128, 16),
+    ("multi-row-g8", [(3000, 2), (17, 2), (600, 1)], 64, 8, 128, 16),
+    ("multi-row-g2-d64", [(2500, 8), (9, 8), (300, 5)], 8, 4, 64, 16),
+    ("multi-row-mha", [(1500, 16), (16, 16), (40, 7)], 4, 4, 128, 16),
+    ("spec-verify-long", [(20000 + 997 * i, 4) for i in range(6)], 32, 8, 128, 16),
+    ("short-and-long-chunks", [(800, 4), (1000, 300), (2000, 1), (90, 3), (513, 64)], 32, 8, 128, 16),
 ]
 
 
@@ -250,7 +258,7 @@ def test_caller_workspace_and_stream(gpu):
     db = DeviceBatch(wl)
     db.append()
     need = pkv.workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
-                               wl.max_blocks_per_seq, wl.block_size)
+                               wl.max_blocks_per_seq, wl.block_size, wl.max_query_len)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
     s = torch.cuda.Stream()
     torch.cuda.synchronize()
