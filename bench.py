@@ -224,6 +224,34 @@ def append_report(pkv, dev, torch, stream):
     return res
 
 
+def graph_report(pkv, c, wl, torch, n=30):
+    """One step (append + attention) captured in a HIP graph and replayed: the per-step
+    time without the Python and launch overhead of the eager calls."""
+    t = c.t
+
+    def body():
+        pkv.kv_append(t["k_new"], t["v_new"], t["slots"], t["kc"], t["vc"])
+        pkv.paged_attention(t["out"], t["q"], t["kc"], t["vc"], t["bt"], t["sl"], t["qsl"], wl.scale,
+                            wl.max_query_len, workspace=t["ws"])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        body()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body()
+    torch.cuda.synchronize()
+    cur = torch.cuda.current_stream()
+    ms = time_calls(g.replay, n, 3, cur, torch)
+    torch.cuda.synchronize()
+    del g
+    return {"graph_step_us_median": round(pct(ms, 50) * 1e3, 3), "graph_step_us_p10": round(pct(ms, 10) * 1e3, 3),
+            "replays": n}
+
+
 def measured_peaks(torch, dev, stream):
     x = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
     x.fill_(1.0)
@@ -362,6 +390,7 @@ def main():
         f"{value:.0f} GB/s step, {achieved:.0f} GB/s attention")
 
     if not args.no_extras:
+        result["graph"] = graph_report(pkv, copies[0], wl, torch)
         if len(pre):
             # the mixed batch itself: decode-only and prefill-only sub-batches
             dms = sub_attention_ms(pkv, base, base.subset(dec), wl.scale, stream, torch)

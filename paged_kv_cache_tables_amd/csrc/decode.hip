@@ -66,7 +66,6 @@ __device__ __forceinline__ SeqInfo seq_info(const AttnParams& p, int s) {
     return SeqInfo{row0, 0, 0, 0};
   return SeqInfo{row0, q, len, (len + kTile - 1) / kTile};
 }
-__device__ __forceinline__ int decode_tiles(const AttnParams& p, int s) { return seq_info(p, s).tiles; }
 
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {

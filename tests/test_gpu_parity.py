@@ -272,3 +272,55 @@ def test_caller_workspace_and_stream(gpu):
     assert np.array_equal(to_host_bits(db.out), got)
     with pytest.raises(pkv.PagedKVError):
         db.attend(workspace=ws[: need - 256])
+
+
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_step_captured_in_hip_graph(gpu, cfg):
+    """append + attention captured once in a HIP graph (the library allocates, memsets and
+    synchronises nothing inside a call), replayed with new queries written in between by
+    eager work: every replay equals the eager call on the same inputs, bit for bit."""
+    torch = gpu
+    import paged_kv_cache_tables_amd as pkv
+    print(f"graph capture config {cfg}", flush=True)
+    wl = W.config0() if cfg == 0 else W.config1(num_seqs=16)
+    db = DeviceBatch(wl)
+    need = pkv.workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                               wl.max_blocks_per_seq, wl.block_size, wl.max_query_len)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    q_alt = [db.q.clone(), torch.flip(db.q, dims=[1]).contiguous(), (db.q * 0.5).contiguous()]
+
+    def eager(qv):
+        db.q.copy_(qv)
+        db.append()
+        db.attend(workspace=ws)
+        torch.cuda.synchronize()
+        return to_host_bits(db.out)
+
+    want = [eager(qv) for qv in q_alt]
+    # the eager result itself is the oracle's (first query set)
+    k2, v2 = oracle_after_append(wl)
+    ref = oracle.paged_attention(wl.q, k2, v2, wl.block_tables, wl.seq_lens, wl.query_start_loc,
+                                 wl.num_kv_heads, wl.scale)
+    compare(want[0], ref, label=f"graph-eager-{cfg}")
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        db.append()
+        db.attend(workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        db.append()
+        db.attend(workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        i = rep % len(q_alt)
+        db.q.copy_(q_alt[i])
+        db.out.zero_()
+        ws.fill_(0xA5)            # stale partials from another call must not leak into this one
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host_bits(db.out), want[i]), f"replay {rep} (query set {i}) differs"
