@@ -10,7 +10,9 @@ arithmetic.
 
 Everything here is plain, slow and meant to be checked by eye against the
 pages it cites: the byte formula, the append as a bit copy, and softmax
-attention written as its definition in float64, walking the block table.
+attention written as its definition in float64, walking the block table; for
+an FP8 cache, the E4M3 code table, nearest-even quantisation with a per-pool
+scale, and the same attention over the dequantised values.
 
 Pins (tests/test_oracle_*.py) tie each function to something other than
 itself: the byte counts the pages print, brute-force scalar attention on
@@ -24,4 +26,12 @@ from .paged import (  # noqa: F401
     kv_append,
     gather_tokens,
     paged_attention,
+)
+from .fp8 import (  # noqa: F401
+    e4m3_value,
+    e4m3_to_f64,
+    f64_to_e4m3,
+    quantize_bf16,
+    kv_append_fp8,
+    paged_attention_fp8,
 )

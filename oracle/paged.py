@@ -135,11 +135,11 @@ def gather_tokens(pool: np.ndarray, table_row: np.ndarray, n_tokens: int) -> np.
 
     [TGI] "Under the Hood: PagedAttention" (the loop over block_table entries
     that fetches each physical block and then each position inside it).
-    Returns bf16 bits, shape [n_tokens, Hkv, D].  Table entries past the last
-    needed block are never read.
+    Returns the pool's element bits (bf16, or FP8 codes), shape [n_tokens, Hkv, D].
+    Table entries past the last needed block are never read.
     """
     bs = pool.shape[1]
-    out = np.empty((n_tokens,) + pool.shape[2:], dtype=np.uint16)
+    out = np.empty((n_tokens,) + pool.shape[2:], dtype=pool.dtype)
     n_blocks = (n_tokens + bs - 1) // bs
     for logical_block in range(n_blocks):
         physical = int(table_row[logical_block])

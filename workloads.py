@@ -34,7 +34,7 @@ BF16_PINF = np.uint16(0x7F80)
 BF16_NINF = np.uint16(0xFF80)
 
 # SeedSequence stream ids (entropy = [seed, config id, stream, ...])
-_S_LENGTHS, _S_PLACEMENT, _S_KV, _S_Q, _S_OUTLIER, _S_SHARE, _S_ORDER = range(7)
+_S_LENGTHS, _S_PLACEMENT, _S_KV, _S_Q, _S_OUTLIER, _S_SHARE, _S_ORDER, _S_FP8 = range(8)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -441,3 +441,64 @@ def custom(name: str, seq_specs, Hq: int, Hkv: int, D: int, bs: int, seed: int =
     return _assemble(name, cfg_id, seed, Hq, Hkv, D, bs, seq_specs, num_blocks=num_blocks,
                      row_order=row_order, share=share, placement_seed=placement_seed,
                      poison=poison)
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) pools for the 8-bit cache
+# ---------------------------------------------------------------------------
+
+FP8_NAN = 0x7F     # E4M3 "FN" encoding: S.1111.111 is NaN, there are no infinities
+
+
+@dataclass
+class Fp8Pools:
+    """K and V pools of 8-bit codes [NB, bs, Hkv, D] (uint8) with their per-pool scales.
+    The already-cached rows hold random codes; every other slot holds ``poison``."""
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    k_scale: float
+    v_scale: float
+
+
+def _fp8_code_draws(rng: np.random.Generator, n: int, center: int) -> np.ndarray:
+    """n random E4M3 codes: random sign and mantissa, exponent field spread around
+    ``center`` (a rounded normal with sd 1.5, clipped to 1..15), about 1% with
+    exponent field 0 (zeros and subnormals); never the NaN pattern.  Pure bit
+    drawing: nothing is converted to or from a number."""
+    grid = np.arange(256) + 0.5
+    # exponent field of each 8-bit draw: inverse of a normal CDF sampled on 256 cells
+    from math import erf, sqrt
+    cdf = np.array([0.5 * (1 + erf((e + 0.5 - center) / (1.5 * sqrt(2)))) for e in range(1, 16)])
+    e_of = np.searchsorted(cdf / cdf[-1], grid / 256.0, side="left") + 1
+    e_of = np.minimum(e_of, 15).astype(np.uint8)
+    out = np.empty(n, dtype=np.uint8)
+    step = 1 << 22
+    for a in range(0, n, step):
+        b = min(n, a + step)
+        r = rng.integers(0, 1 << 32, size=b - a, dtype=np.uint32)
+        sign = ((r >> 7) & 1).astype(np.uint8)
+        m = (r & 7).astype(np.uint8)
+        e = e_of[(r >> 8) & 0xFF]
+        e = np.where(((r >> 16) & 0xFF) < 3, np.uint8(0), e)
+        m = np.where(e == 15, np.minimum(m, 6), m)            # keep clear of S.1111.111
+        out[a:b] = (sign << 7) | (e << 3) | m
+    return out
+
+
+def fp8_pools(wl: Workload, k_scale: float = 2.0 ** -4, v_scale: float = 2.0 ** -3,
+              poison: int = FP8_NAN, seed: int = 0) -> Fp8Pools:
+    """8-bit pools with the same block tables, lengths and cached slots as ``wl``.
+    The exponent fields are centred so that code value x scale is of order 1."""
+    shape = (wl.num_blocks, wl.block_size, wl.num_kv_heads, wl.head_dim)
+    cfg = int(wl.meta.get("config", 99))
+    pools = []
+    for which, sc in ((0, k_scale), (1, v_scale)):
+        center = 7 + int(round(-math.log2(sc)))
+        rng = _rng(seed, cfg, _S_FP8, which)
+        pool = np.full(shape, poison, dtype=np.uint8)
+        rows = _fp8_code_draws(rng, wl.cached_slots.size * wl.num_kv_heads * wl.head_dim, center)
+        pool.reshape(-1, wl.num_kv_heads, wl.head_dim)[wl.cached_slots] = rows.reshape(
+            -1, wl.num_kv_heads, wl.head_dim)
+        pools.append(pool)
+    return Fp8Pools(k_cache=pools[0], v_cache=pools[1], k_scale=float(np.float32(k_scale)),
+                    v_scale=float(np.float32(v_scale)))
