@@ -182,6 +182,67 @@ PKV_API int paged_attention(void* out, const void* q, const void* k_cache, const
                     int32_t block_size, float scale, void* workspace, size_t* workspace_bytes,
                     void* stream);
 
+/*
+ * 8-bit (FP8 E4M3) cache.
+ *
+ * [SPEED] "The KV cache: the memory problem that runs the show": quantising the
+ * cache itself to FP8 halves the bytes per token; "Quantization: move fewer
+ * bytes": values are stored in few bits with a shared scale factor and are
+ * dequantised in registers before they are multiplied, so the gain is
+ * bandwidth.  [TGI] "Production Pattern: KV Cache Math": one byte per value
+ * (kv_bytes_per_token(..., 1)).
+ *
+ * Format (a reading; the pages name no encoding): E4M3 without infinities --
+ * sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0
+ * holds the subnormals m * 2^-9; S.1111.111 is NaN; largest magnitude 448.
+ * Scale (a reading; the pages give no convention): one float per pool, K and
+ * V separately, chosen by the caller; a code c in the K pool stands for
+ * value(c) * k_scale.  Pools have the bf16 pools' shape [num_blocks,
+ * block_size, num_kv_heads, head_dim] with one byte per value.
+ */
+
+/*
+ * kv_append_fp8 -- quantise this step's new K and V rows into an 8-bit pool.
+ *
+ * Slot semantics exactly as kv_append.  Every value x of k_new (v_new)
+ * becomes the E4M3 code nearest to y = x / k_scale (x / v_scale), y being the
+ * correctly rounded float32 quotient; an exact tie takes the code with an even
+ * mantissa; |y| >= 448 (and a NaN x) gives the largest finite code of y's
+ * sign (saturation).
+ *
+ *   k_new, v_new   device, bf16 [num_tokens, num_kv_heads, head_dim].
+ *   slot_mapping   device, int64 [num_tokens]; < 0 = padding (skipped).
+ *   k_cache, v_cache  device, uint8 E4M3 pools, written in place.
+ *   head_dim       a multiple of 16 (rows move in 16-byte chunks of codes).
+ *   k_scale, v_scale  finite and > 0 (PKV_EINVAL otherwise).
+ * Returns PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED or PKV_EHIP.
+ */
+PKV_API int kv_append_fp8(const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                  int64_t num_tokens, void* k_cache, void* v_cache, int64_t num_blocks,
+                  int32_t block_size, int32_t num_kv_heads, int32_t head_dim, float k_scale,
+                  float v_scale, void* stream);
+
+/*
+ * paged_attention_fp8 -- paged_attention over 8-bit pools.
+ *
+ * Computes, for the same rows and with the same arguments as paged_attention,
+ * the softmax attention of the dequantised rows value(code) * k_scale and
+ * value(code) * v_scale.  The kernels widen codes exactly to bf16 (every E4M3
+ * value is a bf16 value), fold k_scale into the score scale and v_scale into
+ * the output; accumulation is fp32 and out is bf16 as for bf16 pools.  The
+ * workspace is the one paged_attention needs for the same shapes (query it
+ * with workspace == NULL here or there).  head_dim 64 needs block_size 16 or
+ * 32 (PKV_EUNSUPPORTED for 8).  k_scale, v_scale finite and > 0.
+ * Returns PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE or PKV_EHIP.
+ */
+PKV_API int paged_attention_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, const int32_t* seq_lens,
+                        const int32_t* query_start_loc, int32_t num_seqs, int64_t num_q_tokens,
+                        int32_t max_blocks_per_seq, int32_t max_query_len, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                        int32_t block_size, float scale, float k_scale, float v_scale,
+                        void* workspace, size_t* workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static string). */
 PKV_API const char* pkv_status_string(int status);
 

@@ -50,6 +50,14 @@ def load_library() -> ctypes.CDLL:
     lib.paged_attention.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                     c_void_p, c_int32, c_int64, c_int32, c_int32, c_int32, c_int32,
                                     c_int32, c_int64, c_int32, c_float, c_void_p, c_size_p, c_void_p]
+    lib.kv_append_fp8.restype = c_int
+    lib.kv_append_fp8.argtypes = [c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_int64,
+                                  c_int32, c_int32, c_int32, c_float, c_float, c_void_p]
+    lib.paged_attention_fp8.restype = c_int
+    lib.paged_attention_fp8.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                        c_void_p, c_int32, c_int64, c_int32, c_int32, c_int32, c_int32,
+                                        c_int32, c_int64, c_int32, c_float, c_float, c_float, c_void_p,
+                                        c_size_p, c_void_p]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_status_string.argtypes = [c_int]
     _lib = lib
@@ -162,3 +170,78 @@ def paged_attention(out, q, k_cache, v_cache, block_tables, seq_lens, query_star
                              workspace.data_ptr(), ctypes.byref(have), _stream_ptr(stream, dev))
     if st != 0:
         raise PagedKVError("paged_attention", st)
+
+
+def _check_codes(t, name, ndim, device):
+    """An 8-bit pool: uint8 (or torch.float8_e4m3fn) device tensor."""
+    import torch
+    if isinstance(t, torch.Tensor) and t.dtype == torch.float8_e4m3fn:
+        t = t.view(torch.uint8)
+    _check(t, name, torch.uint8, ndim, device)
+    return t
+
+
+def kv_append_fp8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale: float, v_scale: float,
+                  stream=None) -> None:
+    """Quantise new K/V rows [T, Hkv, D] (bf16) into E4M3 pools [NB, bs, Hkv, D] (uint8) at slot_mapping."""
+    import torch
+    dev = k_cache.device
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _check(t, n, torch.bfloat16, 3, dev)
+    k_cache = _check_codes(k_cache, "k_cache", 4, dev)
+    v_cache = _check_codes(v_cache, "v_cache", 4, dev)
+    _check(slot_mapping, "slot_mapping", torch.int64, 1, dev)
+    NB, bs, Hkv, D = k_cache.shape
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    T = k_new.shape[0]
+    if k_new.shape != (T, Hkv, D) or v_new.shape != (T, Hkv, D) or slot_mapping.shape[0] != T:
+        raise ValueError("k_new/v_new/slot_mapping shapes do not match the pool")
+    st = load_library().kv_append_fp8(k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(), T,
+                                      k_cache.data_ptr(), v_cache.data_ptr(), NB, bs, Hkv, D,
+                                      float(k_scale), float(v_scale), _stream_ptr(stream, dev))
+    if st != 0:
+        raise PagedKVError("kv_append_fp8", st)
+
+
+def paged_attention_fp8(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scale: float,
+                        max_query_len: int, k_scale: float, v_scale: float, workspace=None,
+                        stream=None) -> None:
+    """paged_attention over E4M3 pools (uint8 [NB, bs, Hkv, D]) with per-pool scales k_scale, v_scale.
+    The workspace is sized as for paged_attention (``workspace_bytes``)."""
+    import torch
+    dev = k_cache.device
+    _check(out, "out", torch.bfloat16, 3, dev)
+    _check(q, "q", torch.bfloat16, 3, dev)
+    k_cache = _check_codes(k_cache, "k_cache", 4, dev)
+    v_cache = _check_codes(v_cache, "v_cache", 4, dev)
+    _check(block_tables, "block_tables", torch.int32, 2, dev)
+    _check(seq_lens, "seq_lens", torch.int32, 1, dev)
+    _check(query_start_loc, "query_start_loc", torch.int32, 1, dev)
+    NB, bs, Hkv, D = k_cache.shape
+    T, Hq, Dq = q.shape
+    S = seq_lens.shape[0]
+    if Dq != D or out.shape != q.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("q/out/pool shapes do not match")
+    if query_start_loc.shape[0] != S + 1 or block_tables.shape[0] != S:
+        raise ValueError("query_start_loc must be [S+1] and block_tables [S, max_blocks]")
+    max_blocks = block_tables.shape[1]
+    lib = load_library()
+    need = ctypes.c_size_t(0)
+    st = lib.paged_attention_fp8(None, None, None, None, None, None, None, S, T, max_blocks, max_query_len,
+                                 Hq, Hkv, D, NB, bs, float(scale), float(k_scale), float(v_scale), None,
+                                 ctypes.byref(need), None)
+    if st != 0:
+        raise PagedKVError("paged_attention_fp8", st)
+    if workspace is None:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)
+    else:
+        _check(workspace, "workspace", torch.uint8, 1, dev)
+    have = ctypes.c_size_t(workspace.numel())
+    st = lib.paged_attention_fp8(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                 block_tables.data_ptr(), seq_lens.data_ptr(), query_start_loc.data_ptr(),
+                                 S, T, max_blocks, max_query_len, Hq, Hkv, D, NB, bs, float(scale),
+                                 float(k_scale), float(v_scale), workspace.data_ptr(), ctypes.byref(have),
+                                 _stream_ptr(stream, dev))
+    if st != 0:
+        raise PagedKVError("paged_attention_fp8", st)

@@ -118,20 +118,46 @@ int kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 
-int paged_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
-                    const int32_t* block_tables, const int32_t* seq_lens,
-                    const int32_t* query_start_loc, int32_t num_seqs, int64_t num_q_tokens,
-                    int32_t max_blocks_per_seq, int32_t max_query_len, int32_t num_q_heads,
-                    int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, int32_t block_size,
-                    float scale, void* workspace, size_t* workspace_bytes, void* stream) {
+int kv_append_fp8(const void* k_new, const void* v_new, const int64_t* slot_mapping, int64_t num_tokens,
+                  void* k_cache, void* v_cache, int64_t num_blocks, int32_t block_size,
+                  int32_t num_kv_heads, int32_t head_dim, float k_scale, float v_scale, void* stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return PKV_EINVAL;
+  if (!(isfinite(k_scale) && k_scale > 0.f && isfinite(v_scale) && v_scale > 0.f)) return PKV_EINVAL;
+  if (head_dim % 16 != 0) return PKV_EUNSUPPORTED;  // rows move in 16-byte chunks of codes
+  if (num_blocks > INT64_MAX / block_size) return PKV_EINVAL;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache) return PKV_EINVAL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(slot_mapping, 8))
+    return PKV_EINVAL;
+  const int row_chunks16 = num_kv_heads * head_dim / 16;
+  hipError_t e = pkv::launch_append_fp8(k_new, v_new, slot_mapping, num_tokens, k_cache, v_cache,
+                                        num_blocks * block_size, row_chunks16, k_scale, v_scale,
+                                        (hipStream_t)stream);
+  return e == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+}  // extern "C"
+
+namespace {
+
+// paged_attention and paged_attention_fp8: argument checks, workspace, launches.
+int attention_impl(void* out, const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* block_tables, const int32_t* seq_lens, const int32_t* query_start_loc,
+                   int32_t num_seqs, int64_t num_q_tokens, int32_t max_blocks_per_seq, int32_t max_query_len,
+                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                   int32_t block_size, float scale, bool fp8, float k_scale, float v_scale, void* workspace,
+                   size_t* workspace_bytes, void* stream) {
   if (!workspace_bytes) return PKV_EINVAL;
+  if (fp8 && !(isfinite(k_scale) && k_scale > 0.f && isfinite(v_scale) && v_scale > 0.f)) return PKV_EINVAL;
   if (num_seqs < 0 || num_q_tokens < 0 || max_blocks_per_seq < 1 || max_query_len < 0 ||
       num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0 || block_size <= 0)
     return PKV_EINVAL;
   if (num_q_heads % num_kv_heads != 0) return PKV_EINVAL;
   if (!isfinite(scale)) return PKV_EINVAL;
   const int G = num_q_heads / num_kv_heads;
-  if (!pkv::decode_supported(head_dim, G, block_size) || !pkv::prefill_supported(head_dim, G, block_size))
+  if (!pkv::decode_supported(head_dim, G, block_size, fp8) || !pkv::prefill_supported(head_dim, G, block_size, fp8))
     return PKV_EUNSUPPORTED;
   if (num_seqs > 65535 || num_q_heads > 65535) return PKV_EUNSUPPORTED;   // 16-bit sequence and head counts
   const WsLayout ws = workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
@@ -156,8 +182,8 @@ int paged_attention(void* out, const void* q, const void* k_cache, const void* v
   pkv::AttnParams p{};
   p.out = (uint16_t*)out;
   p.q = (const uint16_t*)q;
-  p.k_cache = (const uint16_t*)k_cache;
-  p.v_cache = (const uint16_t*)v_cache;
+  p.k_cache = (const char*)k_cache;
+  p.v_cache = (const char*)v_cache;
   p.block_tables = block_tables;
   p.seq_lens = seq_lens;
   p.qsl = query_start_loc;
@@ -171,6 +197,8 @@ int paged_attention(void* out, const void* q, const void* k_cache, const void* v
   p.D = head_dim;
   p.bs = block_size;
   p.scale_log2 = scale * 1.4426950408889634f;
+  if (fp8) p.scale_log2 *= k_scale;               // scores of codes, times the K scale
+  p.v_scale = fp8 ? v_scale : 1.f;
   p.decode_waves = decode_waves_for_current_device();
   p.decode_max_q = decode_rows(num_q_heads, num_kv_heads, max_query_len);
   p.min_share_tiles = kMinShareTokens / 64;
@@ -192,10 +220,37 @@ int paged_attention(void* out, const void* q, const void* k_cache, const void* v
   }
 
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = pkv::launch_decode(p, st);
+  hipError_t e = pkv::launch_decode(p, fp8, st);
   if (e == hipSuccess) e = pkv::launch_merge(p, st);
-  if (e == hipSuccess && max_query_len > p.decode_max_q) e = pkv::launch_prefill(p, st);
+  if (e == hipSuccess && max_query_len > p.decode_max_q) e = pkv::launch_prefill(p, fp8, st);
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* seq_lens,
+                    const int32_t* query_start_loc, int32_t num_seqs, int64_t num_q_tokens,
+                    int32_t max_blocks_per_seq, int32_t max_query_len, int32_t num_q_heads,
+                    int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, int32_t block_size,
+                    float scale, void* workspace, size_t* workspace_bytes, void* stream) {
+  return attention_impl(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, num_seqs,
+                        num_q_tokens, max_blocks_per_seq, max_query_len, num_q_heads, num_kv_heads, head_dim,
+                        num_blocks, block_size, scale, false, 1.f, 1.f, workspace, workspace_bytes, stream);
+}
+
+int paged_attention_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* block_tables, const int32_t* seq_lens,
+                        const int32_t* query_start_loc, int32_t num_seqs, int64_t num_q_tokens,
+                        int32_t max_blocks_per_seq, int32_t max_query_len, int32_t num_q_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, int32_t block_size,
+                        float scale, float k_scale, float v_scale, void* workspace, size_t* workspace_bytes,
+                        void* stream) {
+  return attention_impl(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, num_seqs,
+                        num_q_tokens, max_blocks_per_seq, max_query_len, num_q_heads, num_kv_heads, head_dim,
+                        num_blocks, block_size, scale, true, k_scale, v_scale, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

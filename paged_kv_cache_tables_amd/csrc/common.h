@@ -35,6 +35,17 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          c, false);
 }
 
+// 16 E4M3 codes (bytes of v, first code in the low byte of v.x) widened to 16 bf16 values:
+// codes 0..7 into lo, 8..15 into hi, in order.  The conversion is exact (every E4M3 value,
+// subnormals included, is a bf16 value); NaN codes give NaN.  v_cvt_scalef32_pk_bf16_fp8
+// converts the two codes of one 16-bit half of a dword, here with scale 1.
+__device__ __forceinline__ void e4m3x16_to_bf16(uint4 v, uint4& lo, uint4& hi) {
+#define PKV_CVT2(w, high) __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((w), 1.0f, (high)))
+  lo = make_uint4(PKV_CVT2(v.x, false), PKV_CVT2(v.x, true), PKV_CVT2(v.y, false), PKV_CVT2(v.y, true));
+  hi = make_uint4(PKV_CVT2(v.z, false), PKV_CVT2(v.z, true), PKV_CVT2(v.w, false), PKV_CVT2(v.w, true));
+#undef PKV_CVT2
+}
+
 // 2^x with the hardware instruction (results below 2^-126 flush to zero, which for
 // softmax weights relative to a maximum weight of 1 is far below fp32 resolution).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -80,11 +80,16 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 
 // MULTI: some sequence may have several decode rows (decode_max_q > 1); otherwise every
 // column's causal limit is the sequence's last key and only the tile end masks.
-template <int D, int G, int BS, bool MULTI>
+// F8: the pools hold E4M3 codes (one byte per value); rows are widened to bf16 (exactly:
+// every E4M3 value is a bf16 value) on their way into LDS, the K pool scale is folded
+// into the score scale and the V pool scale into the output.
+template <int D, int G, int BS, bool MULTI, bool F8>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void decode_kernel(AttnParams p) {
-  constexpr int CH = D / 8;              // 16-byte chunks per row
-  constexpr int RPI = kWave / CH;        // rows per wave-wide load (4 at d 128)
+  constexpr int CH = D / 8;              // 16-byte bf16 chunks per row in LDS
+  constexpr int EB = F8 ? 1 : 2;         // bytes per pool value
+  constexpr int CHG = D * EB / 16;       // 16-byte chunks per row in the pool
+  constexpr int RPI = kWave / CHG;       // rows per wave-wide load (4 at d 128, 8 for E4M3)
   constexpr int NL = kTile / RPI;        // loads per lane per tile, for K and for V
   constexpr int KS = D / 32;             // k-steps of QK (32 dims each)
   constexpr int DB = D / 16;             // 16-dim blocks of the output
@@ -144,12 +149,12 @@ void decode_kernel(AttnParams p) {
   const int n = lane & 15;                       // accumulator column: query head of the group
   const int kg = lane >> 4;                      // k-group / accumulator row group
   const int Hq = Hkv * G;
-  const size_t row_stride = (size_t)Hkv * D;     // elements per pool slot
+  const size_t row_stride = (size_t)Hkv * D;     // values per pool slot
   const int nblocks = p.num_blocks > 0x7fffffff ? 0x7fffffff : (int)p.num_blocks;
-  const size_t blk_bytes = (size_t)BS * row_stride * 2;
-  const uint32_t row_bytes = (uint32_t)(row_stride * 2);
+  const size_t blk_bytes = (size_t)BS * row_stride * EB;
+  const uint32_t row_bytes = (uint32_t)(row_stride * EB);
   const float c = p.scale_log2;
-  const int lrow = lane / CH, lch = lane % CH;   // this lane's row (within a load) and chunk
+  const int lrow = lane / CHG, lch = lane % CHG; // this lane's row (within a load) and chunk
   const uint32_t lane_off = (uint32_t)lrow * row_bytes + (uint32_t)lch * 16;
 
   // One piece: tiles [tb0, tb1) of (sequence s, KV head h), whose units start at unit a.
@@ -164,8 +169,8 @@ void decode_kernel(AttnParams p) {
     const int t_begin = tb0 * kTile;
     const int t_end = min(tb1 * kTile, L);
     const int* bt_row = p.block_tables + (size_t)s * p.max_blocks;
-    const char* kbase = reinterpret_cast<const char*>(p.k_cache + (size_t)h * D);
-    const char* vbase = reinterpret_cast<const char*>(p.v_cache + (size_t)h * D);
+    const char* kbase = p.k_cache + (size_t)h * D * EB;
+    const char* vbase = p.v_cache + (size_t)h * D * EB;
 
     // ---- Q^T as the B operand: column n, dims ks*32 + kg*8 .. +8 (zero for padding columns) ----
     bf16x8 qreg[KS];
@@ -201,14 +206,22 @@ void decode_kernel(AttnParams p) {
         reg[i] = load_stream16(b + lane_off);
       }
     };
-    // Registers -> LDS, row-major, chunk c of row r at c ^ (r % CH); rows >= nvalid get zeros.
+    // Registers -> LDS, row-major bf16, chunk c of row r at c ^ (r % CH); rows >= nvalid get
+    // zeros.  An E4M3 lane holds 16 codes of its row, which become bf16 chunks 2 lch, 2 lch + 1.
     auto stage = [&](const uint4* reg, int nvalid) {
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const int r = RPI * i + lrow;
         uint4 v = reg[i];
         if (nvalid < kTile && r >= nvalid) v = make_uint4(0u, 0u, 0u, 0u);
-        tile[r][lch ^ (r % CH)] = v;
+        if constexpr (F8) {
+          uint4 lo, hi;
+          e4m3x16_to_bf16(v, lo, hi);
+          tile[r][(2 * lch) ^ (r % CH)] = lo;
+          tile[r][(2 * lch + 1) ^ (r % CH)] = hi;
+        } else {
+          tile[r][lch ^ (r % CH)] = v;
+        }
       }
     };
 
@@ -332,7 +345,7 @@ void decode_kernel(AttnParams p) {
     if (rr_e < cur_q) {
       const int qh = h * G + g_e;
       if (nseg == 1) {                           // the whole (s, h): final output
-        const float inv = 1.f / l_tot;
+        const float inv = F8 ? p.v_scale / l_tot : 1.f / l_tot;
         uint16_t* op = p.out + ((size_t)(row0 + rr_e) * Hq + qh) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
@@ -343,10 +356,11 @@ void decode_kernel(AttnParams p) {
       } else {                                   // partial j = this wave's index among the pieces
         const int j = w - first_w;
         const size_t idx = (((size_t)s * p.decode_max_q + rr_e) * Hq + qh) * p.max_splits + j;
+        const float vs = F8 ? p.v_scale : 1.f;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
           *reinterpret_cast<float4*>(p.ws_o + idx * D + db * 16 + 4 * kg_e) =
-              make_float4(oacc[db][0], oacc[db][1], oacc[db][2], oacc[db][3]);
+              make_float4(oacc[db][0] * vs, oacc[db][1] * vs, oacc[db][2] * vs, oacc[db][3] * vs);
         if (kg_e == 0) { p.ws_m[idx] = m_run; p.ws_l[idx] = l_tot; }
       }
     }
@@ -440,47 +454,58 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(AttnParams p
   }
 }
 
-template <int D, int G, int BS>
+template <int D, int G, int BS, bool F8>
 hipError_t launch_decode_t(const AttnParams& p, hipStream_t stream) {
   if (p.decode_max_q > 1)
-    hipLaunchKernelGGL((decode_kernel<D, G, BS, true>), dim3(p.decode_waves), dim3(kWave), 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<D, G, BS, true, F8>), dim3(p.decode_waves), dim3(kWave), 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_kernel<D, G, BS, false>), dim3(p.decode_waves), dim3(kWave), 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<D, G, BS, false, F8>), dim3(p.decode_waves), dim3(kWave), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, int G>
+// E4M3 rows of d 64 are 64 bytes: a wave-wide load covers 16 rows, more than an 8-slot block.
+template <int D, bool F8>
+constexpr bool decode_bs8_ok() { return !(F8 && D == 64); }
+
+template <int D, int G, bool F8>
 hipError_t dispatch_bs(const AttnParams& p, hipStream_t stream) {
   switch (p.bs) {
-    case 8: return launch_decode_t<D, G, 8>(p, stream);
-    case 16: return launch_decode_t<D, G, 16>(p, stream);
-    case 32: return launch_decode_t<D, G, 32>(p, stream);
+    case 8:
+      if constexpr (decode_bs8_ok<D, F8>()) return launch_decode_t<D, G, 8, F8>(p, stream);
+      break;
+    case 16: return launch_decode_t<D, G, 16, F8>(p, stream);
+    case 32: return launch_decode_t<D, G, 32, F8>(p, stream);
   }
   return hipErrorInvalidValue;
 }
 
-template <int D>
+template <int D, bool F8>
 hipError_t dispatch_g(const AttnParams& p, hipStream_t stream) {
   switch (p.Hq / p.Hkv) {
-    case 1: return dispatch_bs<D, 1>(p, stream);
-    case 2: return dispatch_bs<D, 2>(p, stream);
-    case 4: return dispatch_bs<D, 4>(p, stream);
-    case 8: return dispatch_bs<D, 8>(p, stream);
-    case 16: return dispatch_bs<D, 16>(p, stream);
+    case 1: return dispatch_bs<D, 1, F8>(p, stream);
+    case 2: return dispatch_bs<D, 2, F8>(p, stream);
+    case 4: return dispatch_bs<D, 4, F8>(p, stream);
+    case 8: return dispatch_bs<D, 8, F8>(p, stream);
+    case 16: return dispatch_bs<D, 16, F8>(p, stream);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-bool decode_supported(int D, int G, int bs) {
+bool decode_supported(int D, int G, int bs, bool fp8) {
   return (D == 64 || D == 128) && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16) &&
-         (bs == 8 || bs == 16 || bs == 32);
+         (bs == 8 || bs == 16 || bs == 32) && !(fp8 && D == 64 && bs == 8);
 }
 
-hipError_t launch_decode(const AttnParams& p, hipStream_t stream) {
-  if (p.D == 128) return dispatch_g<128>(p, stream);
-  if (p.D == 64) return dispatch_g<64>(p, stream);
+hipError_t launch_decode(const AttnParams& p, bool fp8, hipStream_t stream) {
+  if (fp8) {
+    if (p.D == 128) return dispatch_g<128, true>(p, stream);
+    if (p.D == 64) return dispatch_g<64, true>(p, stream);
+  } else {
+    if (p.D == 128) return dispatch_g<128, false>(p, stream);
+    if (p.D == 64) return dispatch_g<64, false>(p, stream);
+  }
   return hipErrorInvalidValue;
 }
 

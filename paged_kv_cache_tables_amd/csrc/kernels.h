@@ -10,8 +10,8 @@ namespace pkv {
 struct AttnParams {
   uint16_t* out;                  // bf16 [num_q_tokens, Hq, D]
   const uint16_t* q;              // bf16 [num_q_tokens, Hq, D]
-  const uint16_t* k_cache;        // bf16 [num_blocks, bs, Hkv, D]
-  const uint16_t* v_cache;
+  const char* k_cache;            // [num_blocks, bs, Hkv, D]: bf16, or E4M3 codes (one byte each)
+  const char* v_cache;
   const int32_t* block_tables;    // [num_seqs, max_blocks]
   const int32_t* seq_lens;        // [num_seqs]
   const int32_t* qsl;             // [num_seqs + 1]
@@ -21,7 +21,9 @@ struct AttnParams {
   int max_blocks;
   int max_query_len;
   int Hq, Hkv, D, bs;
-  float scale_log2;               // softmax scale * log2(e): scores live in the exp2 domain
+  float scale_log2;               // softmax scale * log2(e) (* the K pool scale for E4M3 pools):
+                                  // scores live in the exp2 domain
+  float v_scale;                  // E4M3 pools: the V pool scale, applied to the output (1 for bf16)
   int decode_waves;               // decode grid: one wave per resident wave slot of the device
   int decode_max_q;               // sequences with 1 <= q_s <= this are decode rows (q_s x G <= 16)
   int min_share_tiles;            // smallest share of 64-token tiles a decode wave takes
@@ -42,12 +44,17 @@ constexpr int kPrefillPairs = 128;
 hipError_t launch_append(const void* k_new, const void* v_new, const int64_t* slots, int64_t num_tokens,
                          void* k_cache, void* v_cache, int64_t num_slots, int row_chunks,
                          hipStream_t stream);
+// E4M3 pools: row_chunks16 = 16-byte chunks of codes per pool slot (Hkv * D / 16).
+hipError_t launch_append_fp8(const void* k_new, const void* v_new, const int64_t* slots, int64_t num_tokens,
+                             void* k_cache, void* v_cache, int64_t num_slots, int row_chunks16,
+                             float k_scale, float v_scale, hipStream_t stream);
 
-bool decode_supported(int D, int G, int bs);
-hipError_t launch_decode(const AttnParams& p, hipStream_t stream);
+// fp8: the pools hold E4M3 codes instead of bf16.
+bool decode_supported(int D, int G, int bs, bool fp8);
+hipError_t launch_decode(const AttnParams& p, bool fp8, hipStream_t stream);
 hipError_t launch_merge(const AttnParams& p, hipStream_t stream);
 
-bool prefill_supported(int D, int G, int bs);
-hipError_t launch_prefill(const AttnParams& p, hipStream_t stream);
+bool prefill_supported(int D, int G, int bs, bool fp8);
+hipError_t launch_prefill(const AttnParams& p, bool fp8, hipStream_t stream);
 
 }  // namespace pkv

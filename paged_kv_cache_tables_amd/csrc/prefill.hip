@@ -124,6 +124,13 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// s_waitcnt immediate that waits until at most N LDS operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_lds() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt is four bits");
+  __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (N << 8) | (3 << 14));
+}
+
 // Workgroup barrier for LDS hand-over: no memory operation moves across it in the
 // compiler, and unlike __syncthreads() it does not wait for this wave's outstanding
 // global loads (the tiles in flight).  LDS reads before it have been consumed by then.
@@ -133,13 +140,19 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int D, int G>
+// F8: the pools hold E4M3 codes.  Their tiles come through registers instead (16 codes
+// per lane and load, widened exactly to bf16 while they are written to LDS after the
+// current tile's products), the K pool scale is folded into the score scale and the V
+// pool scale into the output.
+template <int D, int G, bool F8>
 __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams p) {
-  constexpr int CH = D / 8;                 // 16-byte chunks per K/V row
+  constexpr int CH = D / 8;                 // 16-byte bf16 chunks per K/V row in LDS
   constexpr int KS = D / 16;                // k-steps of the QK product
   constexpr int DT = D / 32;                // 32-wide dim tiles of the output
   constexpr int ROWS = kPairsPerBlock / G;  // query rows per workgroup
-  constexpr int RW = kWave / CH;            // rows per wave-wide load
+  constexpr int EB = F8 ? 1 : 2;            // bytes per pool value
+  constexpr int CHG = D * EB / 16;          // 16-byte chunks per row in the pool
+  constexpr int RW = kWave / CHG;           // rows per wave-wide load
   constexpr int RB = kWavesP * RW;          // rows per workgroup-wide load
   constexpr int NLD = kKT / RB;             // loads per thread per tile, for K and for V
   static_assert(kKT % RB == 0, "a tile is a whole number of workgroup-wide loads");
@@ -185,10 +198,10 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
   const int Hq = p.Hkv * G;
   const int* bt_row = p.block_tables + (size_t)s * p.max_blocks;
   const int nblocks = p.num_blocks > 0x7fffffff ? 0x7fffffff : (int)p.num_blocks;
-  const uint32_t row_bytes = (uint32_t)p.Hkv * D * 2;
+  const uint32_t row_bytes = (uint32_t)p.Hkv * D * EB;
   const size_t blk_bytes = (size_t)BS * row_bytes;
-  const char* kbase = reinterpret_cast<const char*>(p.k_cache + (size_t)h * D);
-  const char* vbase = reinterpret_cast<const char*>(p.v_cache + (size_t)h * D);
+  const char* kbase = p.k_cache + (size_t)h * D * EB;
+  const char* vbase = p.v_cache + (size_t)h * D * EB;
 
   // ---- this lane's pair (accumulator / B-operand column n) ----
   const int n = lane & 31;
@@ -242,7 +255,7 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
   // The table entries of a tile come from one vector load (lane j: block kb / BS + j,
   // clamped to the last needed block) issued right after the previous tile's loads, so
   // the wait for that tile covers it; each load then reads its block id with readlane.
-  const int lrow = lane / CH, pc = lane % CH;
+  const int lrow = lane / CHG, pc = lane % CHG;
   const int last_blk = (key_end - 1) >> bs_shift;
   auto fetch_bt = [&](int kb) -> int {
     return bt_row[min((kb >> bs_shift) + lane, last_blk)];
@@ -271,6 +284,39 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
       const int r = RB * i + RW * w + lrow;
       const size_t off = blk_off[i] + src_row[i] * row_bytes + (uint32_t)((pc ^ chunk_swizzle<CH>(r)) * 16);
       __builtin_amdgcn_global_load_lds(vbase + off, (lds_void*)&vd[RB * i + RW * w][0], 16, 0, 0);
+    }
+  };
+
+  // E4M3 tiles: load i of a lane brings the 16 codes of row RB i + RW w + lrow, values
+  // 16 pc .. 16 pc + 15, with the same row choice and clamping as the loads above; they are
+  // written as bf16 chunks 2 pc and 2 pc + 1 of that row (swizzled like every chunk).
+  auto load_regs = [&](int kb, int btv, u32x4 (&kr)[NLD], u32x4 (&vr)[NLD]) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int g_tok = kb + RB * i + RW * w;
+      const int tok = min(g_tok, key_end - 1);
+      const int bl = __builtin_amdgcn_readlane(btv, (tok >> bs_shift) - (kb >> bs_shift));
+      const size_t blk_off = (size_t)((unsigned)bl < (unsigned)nblocks ? bl : 0) * blk_bytes;
+      const uint32_t src_row = (uint32_t)((tok & (BS - 1)) + min(lrow, max(key_end - 1 - g_tok, 0)));
+      const size_t off = blk_off + src_row * row_bytes + (uint32_t)(pc * 16);
+      kr[i] = *reinterpret_cast<const u32x4*>(kbase + off);
+      vr[i] = *reinterpret_cast<const u32x4*>(vbase + off);
+    }
+  };
+  auto store_lds = [&](auto b, const u32x4 (&kr)[NLD], const u32x4 (&vr)[NLD]) {
+    uint4 (*kd)[CH] = kbuf(b);
+    uint4 (*vd)[CH] = vbuf(b);
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int r = RB * i + RW * w + lrow;
+      const int c0 = (2 * pc) ^ chunk_swizzle<CH>(r), c1 = (2 * pc + 1) ^ chunk_swizzle<CH>(r);
+      uint4 lo, hi;
+      e4m3x16_to_bf16(make_uint4(kr[i].x, kr[i].y, kr[i].z, kr[i].w), lo, hi);
+      kd[r][c0] = lo;
+      kd[r][c1] = hi;
+      e4m3x16_to_bf16(make_uint4(vr[i].x, vr[i].y, vr[i].z, vr[i].w), lo, hi);
+      vd[r][c0] = lo;
+      vd[r][c1] = hi;
     }
   };
 
@@ -398,23 +444,52 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
   // Per thread, a tile is 2 NLD loads (K then V) issued in tile order, so "tile t has
   // landed" is "at most the loads of the tiles issued after it are outstanding".
   const int ntiles = (key_end + kKT - 1) / kKT;
-  int btv = fetch_bt(0);
-  issue(IntC<0>(), 0, btv);
-  if (ntiles > 1) btv = fetch_bt(kKT);
-  auto step = [&](auto b, int t) {
-    constexpr int B = decltype(b)::value;
-    const int kb = t * kKT;
-    wait_vmem<0>();                              // this thread's part of tile t (and the next table entries) landed
-    lds_barrier();                               // all of tile t visible; buffer (t+1) % 2 no longer read
-    if (t + 1 < ntiles) {
-      issue(IntC<(B + 1) % kBuf>(), kb + kKT, btv);
-      if (t + 2 < ntiles) btv = fetch_bt(kb + 2 * kKT);
+  if constexpr (!F8) {
+    int btv = fetch_bt(0);
+    issue(IntC<0>(), 0, btv);
+    if (ntiles > 1) btv = fetch_bt(kKT);
+    auto step = [&](auto b, int t) {
+      constexpr int B = decltype(b)::value;
+      const int kb = t * kKT;
+      wait_vmem<0>();                            // this thread's part of tile t (and the next table entries) landed
+      lds_barrier();                             // all of tile t visible; buffer (t+1) % 2 no longer read
+      if (t + 1 < ntiles) {
+        issue(IntC<(B + 1) % kBuf>(), kb + kKT, btv);
+        if (t + 2 < ntiles) btv = fetch_bt(kb + 2 * kKT);
+      }
+      if (wave_active && kb <= wave_lim_max) tile_compute(b, kb);
+    };
+    for (int t = 0; t < ntiles; t += kBuf) {
+      step(IntC<0>(), t);
+      if (t + 1 < ntiles) step(IntC<1>(), t + 1);
     }
-    if (wave_active && kb <= wave_lim_max) tile_compute(b, kb);
-  };
-  for (int t = 0; t < ntiles; t += kBuf) {
-    step(IntC<0>(), t);
-    if (t + 1 < ntiles) step(IntC<1>(), t + 1);
+  } else {
+    // E4M3: tile t + 1 is loaded into registers during step t and written to LDS after
+    // tile t's products; the barrier that opens step t + 1 makes it visible.
+    (void)issue;
+    int btv = fetch_bt(0);
+    {
+      u32x4 kr[NLD], vr[NLD];
+      load_regs(0, btv, kr, vr);
+      store_lds(IntC<0>(), kr, vr);
+    }
+    if (ntiles > 1) btv = fetch_bt(kKT);
+    auto step = [&](auto b, int t) {
+      constexpr int B = decltype(b)::value;
+      const int kb = t * kKT;
+      wait_lds<0>();                             // this wave's writes of tile t are done
+      lds_barrier();                             // all of tile t visible; buffer (t+1) % 2 no longer read
+      const bool more = t + 1 < ntiles;
+      u32x4 kr[NLD], vr[NLD];
+      if (more) load_regs(kb + kKT, btv, kr, vr);
+      if (t + 2 < ntiles) btv = fetch_bt(kb + 2 * kKT);
+      if (wave_active && kb <= wave_lim_max) tile_compute(b, kb);
+      if (more) store_lds(IntC<(B + 1) % kBuf>(), kr, vr);
+    };
+    for (int t = 0; t < ntiles; t += kBuf) {
+      step(IntC<0>(), t);
+      if (t + 1 < ntiles) step(IntC<1>(), t + 1);
+    }
   }
 
   // ---- finish: O / l, bf16 out; lane holds dims 32 dt + 8 q + 4 kg + 0..3 of its pair ----
@@ -422,7 +497,7 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
   const auto sw = __builtin_amdgcn_permlane32_swap(x, x, false, false);
   const float l_tot = __int_as_float(sw[0]) + __int_as_float(sw[1]);
   if (!pvalid) return;
-  const float inv = 1.f / l_tot;
+  const float inv = F8 ? p.v_scale / l_tot : 1.f / l_tot;
   uint16_t* op = p.out + ((size_t)(row0 + jrow) * Hq + (size_t)h * G + gq) * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
@@ -437,7 +512,7 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
     }
 }
 
-template <int D>
+template <int D, bool F8>
 hipError_t dispatch_g(const AttnParams& p, hipStream_t stream) {
   const int G = p.Hq / p.Hkv;
   const int rows = kPairsPerBlock / G;
@@ -449,11 +524,11 @@ hipError_t dispatch_g(const AttnParams& p, hipStream_t stream) {
   const int64_t n = ((int64_t)p.Hkv * p.plan_stride + 7) / 8 * 8;
   dim3 grid((unsigned)n);
   switch (G) {
-    case 1: hipLaunchKernelGGL((prefill_kernel<D, 1>), grid, dim3(kWavesP * kWave), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((prefill_kernel<D, 2>), grid, dim3(kWavesP * kWave), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((prefill_kernel<D, 4>), grid, dim3(kWavesP * kWave), 0, stream, p); break;
-    case 8: hipLaunchKernelGGL((prefill_kernel<D, 8>), grid, dim3(kWavesP * kWave), 0, stream, p); break;
-    case 16: hipLaunchKernelGGL((prefill_kernel<D, 16>), grid, dim3(kWavesP * kWave), 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((prefill_kernel<D, 1, F8>), grid, dim3(kWavesP * kWave), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((prefill_kernel<D, 2, F8>), grid, dim3(kWavesP * kWave), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((prefill_kernel<D, 4, F8>), grid, dim3(kWavesP * kWave), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((prefill_kernel<D, 8, F8>), grid, dim3(kWavesP * kWave), 0, stream, p); break;
+    case 16: hipLaunchKernelGGL((prefill_kernel<D, 16, F8>), grid, dim3(kWavesP * kWave), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -461,17 +536,23 @@ hipError_t dispatch_g(const AttnParams& p, hipStream_t stream) {
 
 }  // namespace
 
-bool prefill_supported(int D, int G, int bs) {
-  // a wave-wide tile load (64 / (D / 8) rows) must stay inside one pool block, and a
-  // tile (64 keys) must hold whole blocks
+bool prefill_supported(int D, int G, int bs, bool fp8) {
+  // a wave-wide tile load (64 / (16-byte chunks per pool row) rows) must stay inside one
+  // pool block, and a tile (64 keys) must hold whole blocks
+  const int chunks = D * (fp8 ? 1 : 2) / 16;
   return (D == 64 || D == 128) && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16) &&
-         (bs == 8 || bs == 16 || bs == 32) && bs % (kWave / (D / 8)) == 0;
+         (bs == 8 || bs == 16 || bs == 32) && bs % (kWave / chunks) == 0;
 }
 
-hipError_t launch_prefill(const AttnParams& p, hipStream_t stream) {
+hipError_t launch_prefill(const AttnParams& p, bool fp8, hipStream_t stream) {
   if (p.max_query_len <= p.decode_max_q) return hipSuccess;   // decode rows only
-  if (p.D == 128) return dispatch_g<128>(p, stream);
-  if (p.D == 64) return dispatch_g<64>(p, stream);
+  if (fp8) {
+    if (p.D == 128) return dispatch_g<128, true>(p, stream);
+    if (p.D == 64) return dispatch_g<64, true>(p, stream);
+  } else {
+    if (p.D == 128) return dispatch_g<128, false>(p, stream);
+    if (p.D == 64) return dispatch_g<64, false>(p, stream);
+  }
   return hipErrorInvalidValue;
 }
 

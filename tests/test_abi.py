@@ -139,3 +139,70 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "PKG", str(tmp_path))
     with pytest.raises(FileNotFoundError):
         _lib.kv_bytes_per_token(1, 1, 1, 1)
+
+
+# -- 8-bit cache ---------------------------------------------------------------
+
+def append_fp8_args(**over):
+    a = dict(k_new=FAKE, v_new=FAKE, slot_mapping=FAKE, num_tokens=4, k_cache=FAKE, v_cache=FAKE,
+             num_blocks=8, block_size=16, num_kv_heads=2, head_dim=64, k_scale=0.5, v_scale=0.25, stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(k_new=None), PKV_EINVAL),
+    (dict(num_tokens=-1), PKV_EINVAL),
+    (dict(k_scale=0.0), PKV_EINVAL),
+    (dict(v_scale=-1.0), PKV_EINVAL),
+    (dict(k_scale=float("inf")), PKV_EINVAL),
+    (dict(v_scale=float("nan")), PKV_EINVAL),
+    (dict(head_dim=72), PKV_EUNSUPPORTED),          # rows of codes move in 16-byte chunks
+    (dict(v_cache=FAKE + 8), PKV_EINVAL),
+    (dict(num_tokens=0, k_new=None, slot_mapping=None), PKV_OK),
+])
+def test_kv_append_fp8_validation(lib, over, expect):
+    assert lib.kv_append_fp8(*append_fp8_args(**over)) == expect
+
+
+def attn_fp8_args(**over):
+    n = ctypes.c_size_t(1 << 30)
+    a = dict(out=FAKE, q=FAKE, k_cache=FAKE, v_cache=FAKE, block_tables=FAKE, seq_lens=FAKE,
+             qsl=FAKE, num_seqs=4, num_q_tokens=8, max_blocks=4, max_query_len=5, Hq=4, Hkv=2, D=64,
+             num_blocks=64, bs=16, scale=0.125, k_scale=0.5, v_scale=0.25, workspace=None,
+             workspace_bytes=ctypes.byref(n), stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+def test_fp8_workspace_matches_bf16(lib):
+    for shape in (dict(), dict(D=128, Hq=32, Hkv=8, max_query_len=1), dict(bs=32, max_query_len=300)):
+        a, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+        assert lib.paged_attention_fp8(*attn_fp8_args(workspace_bytes=ctypes.byref(a), **shape)) == PKV_OK
+        assert lib.paged_attention(*attn_args(workspace_bytes=ctypes.byref(b), **shape)) == PKV_OK
+        assert a.value == b.value > 0
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(k_scale=0.0), PKV_EINVAL),
+    (dict(v_scale=float("nan")), PKV_EINVAL),
+    (dict(k_scale=-2.0), PKV_EINVAL),
+    (dict(bs=8), PKV_EUNSUPPORTED),                 # d 64 codes: a wave-wide load spans 16 slots
+    (dict(D=96), PKV_EUNSUPPORTED),
+    (dict(Hq=6, Hkv=4), PKV_EINVAL),
+    (dict(scale=float("inf")), PKV_EINVAL),
+])
+def test_paged_attention_fp8_validation(lib, over, expect):
+    assert lib.paged_attention_fp8(*attn_fp8_args(**over)) == expect
+
+
+def test_paged_attention_fp8_accepts_d128_bs8(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.paged_attention_fp8(*attn_fp8_args(D=128, bs=8, workspace_bytes=ctypes.byref(n))) == PKV_OK
+
+
+def test_paged_attention_fp8_checks_pointers_before_launch(lib):
+    n = ctypes.c_size_t(1 << 30)
+    for field in ("out", "q", "k_cache", "v_cache", "block_tables", "seq_lens", "qsl"):
+        args = attn_fp8_args(workspace=FAKE, workspace_bytes=ctypes.byref(n), **{field: None})
+        assert lib.paged_attention_fp8(*args) == PKV_EINVAL, field

@@ -461,16 +461,19 @@ class Fp8Pools:
 
 
 def _fp8_code_draws(rng: np.random.Generator, n: int, center: int) -> np.ndarray:
-    """n random E4M3 codes: random sign and mantissa, exponent field spread around
-    ``center`` (a rounded normal with sd 1.5, clipped to 1..15), about 1% with
-    exponent field 0 (zeros and subnormals); never the NaN pattern.  Pure bit
-    drawing: nothing is converted to or from a number."""
+    """n random E4M3 codes: random sign and mantissa, exponent field spread below
+    ``center`` (a rounded normal with mean center - 1 and sd 1, clipped to
+    1..center + 1, so magnitudes stay under 4 times 2^(center - 7) the way N(0,1)
+    draws stay under a few units), about 1% with exponent field 0 (zeros and
+    subnormals); never the NaN pattern.  Pure bit drawing: nothing is converted to or
+    from a number."""
     grid = np.arange(256) + 0.5
+    top = min(15, center + 1)
     # exponent field of each 8-bit draw: inverse of a normal CDF sampled on 256 cells
     from math import erf, sqrt
-    cdf = np.array([0.5 * (1 + erf((e + 0.5 - center) / (1.5 * sqrt(2)))) for e in range(1, 16)])
+    cdf = np.array([0.5 * (1 + erf((e + 0.5 - (center - 1)) / sqrt(2))) for e in range(1, top + 1)])
     e_of = np.searchsorted(cdf / cdf[-1], grid / 256.0, side="left") + 1
-    e_of = np.minimum(e_of, 15).astype(np.uint8)
+    e_of = np.minimum(e_of, top).astype(np.uint8)
     out = np.empty(n, dtype=np.uint8)
     step = 1 << 22
     for a in range(0, n, step):
