@@ -84,8 +84,9 @@ def pct(xs, q):
     return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
 
 
-def cpu_baseline(wl, k2, v2, budget_s: float):
-    """Time the float64 oracle (as it stands) on whole sequences of the batch until the budget is used."""
+def cpu_baseline(wl, k2, v2, budget_s: float, f8=None):
+    """Time the float64 oracle (as it stands) on whole sequences of the batch until the budget is used
+    (with ``f8``: the 8-bit pools' oracle; bytes then count one per value)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -102,10 +103,14 @@ def cpu_baseline(wl, k2, v2, budget_s: float):
             rows = list(range(int(qsl[s]), int(qsl[s + 1])))
             if not rows:
                 continue
-            oracle.paged_attention(wl.q, k2, v2, wl.block_tables, wl.seq_lens, wl.query_start_loc,
-                                   wl.num_kv_heads, wl.scale, rows=rows)
+            if f8 is None:
+                oracle.paged_attention(wl.q, k2, v2, wl.block_tables, wl.seq_lens, wl.query_start_loc,
+                                       wl.num_kv_heads, wl.scale, rows=rows)
+            else:
+                oracle.paged_attention_fp8(wl.q, k2, v2, wl.block_tables, wl.seq_lens, wl.query_start_loc,
+                                           wl.num_kv_heads, wl.scale, f8.k_scale, f8.v_scale, rows=rows)
             seqs += 1
-            bytes_done += wl.kv_read_bytes([s])
+            bytes_done += wl.kv_read_bytes([s]) // (1 if f8 is None else 2)
             t_used = time.perf_counter() - t0
             if t_used >= budget_s:
                 break
@@ -252,6 +257,77 @@ def graph_report(pkv, c, wl, torch, n=30):
             "replays": n}
 
 
+def fp8_report(pkv, d, torch, stream, bf16_call_us, n=30, copies=3):
+    """The same batch over 8-bit (E4M3) pools: kv_append_fp8 of the step's tokens, then
+    paged_attention_fp8 timed like the bf16 call (copies cycled); GB/s of the code bytes."""
+    import workloads
+    wl = d.wl
+    f8 = workloads.fp8_pools(wl)
+    t = d.t
+    pools = []
+    for i in range(copies):
+        kc = torch.from_numpy(f8.k_cache).to(d.dev)
+        vc = torch.from_numpy(f8.v_cache).to(d.dev)
+        pkv.kv_append_fp8(t["k_new"], t["v_new"], t["slots"], kc, vc, f8.k_scale, f8.v_scale, stream=stream)
+        pools.append((kc, vc))
+    out = torch.empty_like(t["q"])
+    ws = torch.empty(pkv.workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                         wl.max_blocks_per_seq, wl.block_size, wl.max_query_len),
+                     dtype=torch.uint8, device=d.dev)
+    it = [0]
+
+    def call():
+        kc, vc = pools[it[0] % copies]
+        it[0] += 1
+        pkv.paged_attention_fp8(out, t["q"], kc, vc, t["bt"], t["sl"], t["qsl"], wl.scale, wl.max_query_len,
+                                f8.k_scale, f8.v_scale, workspace=ws, stream=stream)
+    ms = time_calls(call, n, 3, stream, torch)
+    med = pct(ms, 50)
+    code_bytes = wl.kv_read_bytes() // 2
+    uniq = wl.unique_kv_read_bytes() // 2
+    # the append of the step's new tokens alone
+    kc, vc = pools[0]
+    ams = time_calls(lambda: pkv.kv_append_fp8(t["k_new"], t["v_new"], t["slots"], kc, vc, f8.k_scale,
+                                               f8.v_scale, stream=stream), 20, 3, stream, torch)
+    res = {"workload": workload_desc(wl) + ", E4M3 pools (scales 2^-4, 2^-3)",
+           "kv_code_bytes_per_call": code_bytes, "call_us_median": round(med * 1e3, 3),
+           "call_us_p10": round(pct(ms, 10) * 1e3, 3),
+           "GBps": round(uniq / (med * 1e-3) / 1e9, 1), "frac_of_hbm_peak": round(uniq / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "speedup_vs_bf16_call": round(bf16_call_us / (med * 1e3), 3),
+           "append_fp8_us_median": round(pct(ams, 50) * 1e3, 3)}
+    del pools, out, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def prefill_fp8_report(pkv, d, torch, stream):
+    """The mixed batch's chunked-prefill rows over 8-bit pools, TFLOP/s of causal pairs."""
+    import workloads
+    wl = d.wl
+    f8 = workloads.fp8_pools(wl)
+    kc = torch.from_numpy(f8.k_cache).to(d.dev)
+    vc = torch.from_numpy(f8.v_cache).to(d.dev)
+    t = d.t
+    pkv.kv_append_fp8(t["k_new"], t["v_new"], t["slots"], kc, vc, f8.k_scale, f8.v_scale, stream=stream)
+    pre = wl.prefill_seqs()
+    sub = d.subset(pre)
+    out = torch.empty_like(sub["q"])
+    ws = torch.empty(pkv.workspace_bytes(sub["num_seqs"], wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                         wl.max_blocks_per_seq, wl.block_size, sub["max_query_len"]),
+                     dtype=torch.uint8, device=d.dev)
+
+    def call():
+        pkv.paged_attention_fp8(out, sub["q"], kc, vc, sub["bt"], sub["sl"], sub["qsl"], wl.scale,
+                                sub["max_query_len"], f8.k_scale, f8.v_scale, workspace=ws, stream=stream)
+    ms = time_calls(call, 20, 3, stream, torch)
+    med = pct(ms, 50)
+    flops = 4 * wl.head_dim * wl.num_q_heads * wl.causal_pairs(pre)
+    tf = flops / (med * 1e-3) / 1e12
+    del kc, vc, out, ws
+    torch.cuda.empty_cache()
+    return {"call_us_median": round(med * 1e3, 3), "TFLOPs": round(tf, 1), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+
+
 def measured_peaks(torch, dev, stream):
     x = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
     x.fill_(1.0)
@@ -277,6 +353,9 @@ def main():
     ap.add_argument("--copies", type=int, default=3, help="device copies of the batch cycled per step")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
+                    help="cache element type of the timed step: bf16 (default) or 8-bit E4M3 codes with "
+                         "per-pool scales (kv_append_fp8 + paged_attention_fp8; implies --no-extras)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the prefill, append and peak measurements (step timing and roofline only)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -313,6 +392,13 @@ def main():
     log(f"generating config {args.config} ...")
     wl = workloads.make_config(args.config)
     base = Device(wl, dev, torch)
+    fp8 = args.kv == "fp8"
+    if fp8:
+        args.no_extras = True
+        f8 = workloads.fp8_pools(wl)
+        wl.drop_pools()
+        base.t["kc"] = torch.from_numpy(f8.k_cache).to(dev)
+        base.t["vc"] = torch.from_numpy(f8.v_cache).to(dev)
     copies = [base] + [base.clone() for _ in range(args.copies - 1)]
     ws_bytes = pkv.workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
                                    wl.max_blocks_per_seq, wl.block_size, wl.max_query_len)
@@ -323,12 +409,20 @@ def main():
 
     def append(c):
         t = c.t
-        pkv.kv_append(t["k_new"], t["v_new"], t["slots"], t["kc"], t["vc"], stream=stream)
+        if fp8:
+            pkv.kv_append_fp8(t["k_new"], t["v_new"], t["slots"], t["kc"], t["vc"], f8.k_scale, f8.v_scale,
+                              stream=stream)
+        else:
+            pkv.kv_append(t["k_new"], t["v_new"], t["slots"], t["kc"], t["vc"], stream=stream)
 
     def attend(c):
         t = c.t
-        pkv.paged_attention(t["out"], t["q"], t["kc"], t["vc"], t["bt"], t["sl"], t["qsl"], wl.scale,
-                            wl.max_query_len, workspace=t["ws"], stream=stream)
+        if fp8:
+            pkv.paged_attention_fp8(t["out"], t["q"], t["kc"], t["vc"], t["bt"], t["sl"], t["qsl"], wl.scale,
+                                    wl.max_query_len, f8.k_scale, f8.v_scale, workspace=t["ws"], stream=stream)
+        else:
+            pkv.paged_attention(t["out"], t["q"], t["kc"], t["vc"], t["bt"], t["sl"], t["qsl"], wl.scale,
+                                wl.max_query_len, workspace=t["ws"], stream=stream)
 
     for i in range(args.warmup):
         append(copies[i % len(copies)])
@@ -350,8 +444,8 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     attn_ms = [a.elapsed_time(b) for a, b in evs]
     attn_avg_ms = float(np.mean(attn_ms))
-    kv_bytes = wl.kv_read_bytes()
-    uniq_bytes = wl.unique_kv_read_bytes()
+    kv_bytes = wl.kv_read_bytes() // (2 if fp8 else 1)          # one byte per value for E4M3 pools
+    uniq_bytes = wl.unique_kv_read_bytes() // (2 if fp8 else 1)
     dec = wl.decode_seqs()
     pre = wl.prefill_seqs()
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
@@ -369,19 +463,21 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16 (E4M3 K/V cache)" if fp8 else "bf16",
         "data": "synthetic",
         "config": {"workload": workload_desc(wl), "config_index": args.config, "seed": wl.meta["seed"],
                    "kv_bytes_per_step": kv_bytes, "unique_kv_bytes_per_step": uniq_bytes,
                    "decode_rows": int(len(dec)), "prefill_rows": int(wl.query_lens[pre].sum()) if len(pre) else 0,
-                   "appended_tokens": wl.num_q_tokens, "device_copies_cycled": len(copies)},
+                   "appended_tokens": wl.num_q_tokens, "device_copies_cycled": len(copies),
+                   "kv_cache": "e4m3, per-pool scales 2^-4 (K), 2^-3 (V)" if fp8 else "bf16"},
         "decode_tokens_per_s": round(len(dec) / (ms_per_step * 1e-3), 1),
-        "roofline": {"bound": "hbm", "kernel": "paged_attention call (split-K decode + LSE merge"
+        "roofline": {"bound": "hbm", "kernel": ("paged_attention_fp8" if fp8 else "paged_attention")
+                     + " call (split-K decode + LSE merge"
                      + (" + prefill" if len(pre) else "") + ")",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "avg_call_us": round(attn_avg_ms * 1e3, 3),
                      "algorithmic_bytes_per_call": uniq_bytes,
-                     "traffic": traffic_from_profile(args.config, "paged_attention")},
+                     "traffic": traffic_from_profile(args.config, "paged_attention_fp8" if fp8 else "paged_attention")},
         "call_us": {"median": round(pct(attn_ms, 50) * 1e3, 3), "p10": round(pct(attn_ms, 10) * 1e3, 3),
                     "p90": round(pct(attn_ms, 90) * 1e3, 3),
                     "hot_cache_median": round(pct(hot_ms, 50) * 1e3, 3)},
@@ -391,6 +487,8 @@ def main():
 
     if not args.no_extras:
         result["graph"] = graph_report(pkv, copies[0], wl, torch)
+        log("8-bit pools ...")
+        result["fp8"] = fp8_report(pkv, base, torch, stream, result["call_us"]["median"])
         if len(pre):
             # the mixed batch itself: decode-only and prefill-only sub-batches
             dms = sub_attention_ms(pkv, base, base.subset(dec), wl.scale, stream, torch)
@@ -401,6 +499,7 @@ def main():
                                "decode_only_logical_GBps": round(wl.kv_read_bytes(dec) / (dmed * 1e-3) / 1e9, 1),
                                "mixed_call_us_median": result["call_us"]["median"]}
             result["prefill"] = prefill_report(pkv, base, stream, torch)
+            result["prefill"]["fp8"] = prefill_fp8_report(pkv, base, torch, stream)
             result["mixed"]["prefill_only_call_us_median"] = result["prefill"]["call_us_median"]
             del copies
         else:
@@ -412,6 +511,7 @@ def main():
             # the pools must hold this step's tokens before attention reads them
             pkv.kv_append(d3.t["k_new"], d3.t["v_new"], d3.t["slots"], d3.t["kc"], d3.t["vc"], stream=stream)
             result["prefill"] = prefill_report(pkv, d3, stream, torch)
+            result["prefill"]["fp8"] = prefill_fp8_report(pkv, d3, torch, stream)
             del d3
         torch.cuda.empty_cache()
         result["append"] = append_report(pkv, dev, torch, stream)
@@ -424,8 +524,13 @@ def main():
 
     if not args.no_cpu:
         import oracle
-        k2, v2 = oracle.kv_append(wl.k_cache, wl.v_cache, wl.k_new, wl.v_new, wl.slot_mapping)
-        result["cpu_baseline"] = cpu_baseline(wl, k2, v2, args.cpu_budget)
+        if fp8:
+            k2, v2 = oracle.kv_append_fp8(f8.k_cache, f8.v_cache, wl.k_new, wl.v_new, wl.slot_mapping,
+                                          f8.k_scale, f8.v_scale)
+            result["cpu_baseline"] = cpu_baseline(wl, k2, v2, args.cpu_budget, f8)
+        else:
+            k2, v2 = oracle.kv_append(wl.k_cache, wl.v_cache, wl.k_new, wl.v_new, wl.slot_mapping)
+            result["cpu_baseline"] = cpu_baseline(wl, k2, v2, args.cpu_budget)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
