@@ -69,6 +69,7 @@ extern "C" {
 #define PKV_EUNSUPPORTED (-2) /* a shape the kernels are not built for             */
 #define PKV_EWORKSPACE   (-3) /* workspace too small (see paged_attention)         */
 #define PKV_EHIP         (-4) /* a HIP launch reported an error                    */
+#define PKV_ENOSPACE     (-5) /* allocator: not enough blocks even after eviction   */
 
 /*
  * kv_bytes_per_token -- bytes of K plus V that one token occupies in the cache.
@@ -242,6 +243,101 @@ PKV_API int paged_attention_fp8(void* out, const void* q, const void* k_cache, c
                         int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
                         int32_t block_size, float scale, float k_scale, float v_scale,
                         void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * kv_copy_blocks -- copy whole pool blocks, K and V (copy-on-write).
+ *
+ * [TGI] "Under the Hood: PagedAttention", "Prefix sharing": when a sequence
+ * writes into a block it shares, the block is first copied to a new physical
+ * block and the writer's table points there.  For every i < n_pairs with
+ * src[i] != dst[i] and both in [0, num_blocks): block dst[i] of k_cache and of
+ * v_cache becomes a bit copy of block src[i].  Pairs outside the pool are
+ * skipped.  Works for bf16 and 8-bit pools (elem_bytes 2 or 1).
+ *
+ *   k_cache, v_cache  device pools [num_blocks, block_size, num_kv_heads, head_dim].
+ *   src, dst       device, int32 [n_pairs]; the dst blocks are distinct and
+ *                  none is a src of the same call (otherwise the result is
+ *                  unspecified).
+ *   n_pairs        >= 0 (0 enqueues nothing).
+ *   block_size * num_kv_heads * head_dim * elem_bytes must be a multiple of 16.
+ * Returns PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED or PKV_EHIP.
+ */
+PKV_API int kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst,
+                   int32_t n_pairs, int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t elem_bytes, void* stream);
+
+/*
+ * Host block allocator with a radix prefix cache.
+ *
+ * [V3] "The radix prefix cache": the scheduler owns a block allocator that
+ * keeps block 0 back, a free list, and a compressed radix tree of cached
+ * prefixes keyed by token ids at block granularity.  Allocating walks the
+ * tree with the prompt, references the deepest matched node before anything
+ * can be evicted, and takes fresh blocks for the rest, evicting the least
+ * recently used unreferenced prefixes when the free list runs dry; freeing
+ * drops the reference and inserts the computed prefix (splitting an edge
+ * where tokens diverge), returning blocks that another request cached in the
+ * meantime.  [V3] "Inside the batching task": a prompt always keeps one token
+ * to compute.  [TGI] "Prefix sharing": shared blocks are copied on write.
+ * The tables and slots it returns feed kv_append / paged_attention.
+ *
+ * Readings (the pages are silent): only whole blocks are cached and matched
+ * (at most floor((n_prompt - 1) / block_size) blocks of a prompt); fresh
+ * blocks are handed out lowest id first; every allocate, free, growing
+ * extend and copying prepare_write advances a clock; eviction removes whole
+ * unreferenced leaves, least recently used first, ties to the oldest node; a
+ * block returns to the free list when no live allocation and no cached
+ * prefix holds it.  Host memory only, no HIP call; not thread-safe (one
+ * caller at a time per allocator).  Every call returns PKV_OK, PKV_EINVAL
+ * (null handle/pointer, unknown id, argument out of range, output capacity
+ * too small -- nothing changed) or PKV_ENOSPACE (nothing changed, except the
+ * clock and a tree split that does not change any cached content).
+ */
+typedef struct pkv_allocator pkv_allocator;
+
+/* num_blocks >= 2 (block 0 is never handed out), block_size >= 1; NULL on error. */
+PKV_API pkv_allocator* pkv_allocator_create(int32_t num_blocks, int32_t block_size);
+PKV_API void pkv_allocator_destroy(pkv_allocator* a);
+
+/* Blocks for a request with prompt tokens[0..n_tokens) that will hold n_total >= max(1,
+ * n_tokens) tokens.  Writes its id, its ceil(n_total / block_size) blocks (cached prefix
+ * first) into blocks[0..capacity) with the count in *n_blocks, and in *prefix_len the number
+ * of prompt tokens whose K/V is already cached (a multiple of block_size). */
+PKV_API int pkv_allocator_allocate(pkv_allocator* a, const int32_t* tokens, int32_t n_tokens,
+                           int32_t n_total, int64_t* alloc_id, int32_t* blocks, int32_t capacity,
+                           int32_t* n_blocks, int32_t* prefix_len);
+
+/* End an allocation whose K/V now holds tokens[0..n_tokens); its whole blocks are cached. */
+PKV_API int pkv_allocator_free(pkv_allocator* a, int64_t alloc_id, const int32_t* tokens,
+                       int32_t n_tokens);
+
+/* A new allocation sharing the blocks that hold the first n_tokens tokens of alloc_id
+ * (blocks may be NULL: only the id and count are returned). */
+PKV_API int pkv_allocator_fork(pkv_allocator* a, int64_t alloc_id, int32_t n_tokens, int64_t* new_id,
+                       int32_t* blocks, int32_t capacity, int32_t* n_blocks);
+
+/* Grow an allocation to hold n_total tokens (fresh blocks at its end); returns its table. */
+PKV_API int pkv_allocator_extend(pkv_allocator* a, int64_t alloc_id, int32_t n_total, int32_t* blocks,
+                         int32_t capacity, int32_t* n_blocks);
+
+/* Call before writing token position pos.  If its block is shared, the allocation gets a
+ * fresh block instead and *src, *dst name the block copy the caller must make on the
+ * device (kv_copy_blocks) before the write; otherwise *src = *dst = -1. */
+PKV_API int pkv_allocator_prepare_write(pkv_allocator* a, int64_t alloc_id, int32_t pos, int32_t* src,
+                                int32_t* dst);
+
+/* slots[i] = block of position start + i times block_size plus its offset (kv_append's
+ * slot_mapping); positions must lie inside the allocation. */
+PKV_API int pkv_allocator_slots(pkv_allocator* a, int64_t alloc_id, int32_t start, int32_t count,
+                        int64_t* slots);
+
+/* The allocation's block table (a row of paged_attention's block_tables). */
+PKV_API int pkv_allocator_table(pkv_allocator* a, int64_t alloc_id, int32_t* blocks, int32_t capacity,
+                        int32_t* n_blocks);
+
+/* Free blocks, and blocks held by cached prefixes (-1 for a NULL handle). */
+PKV_API int32_t pkv_allocator_num_free(const pkv_allocator* a);
+PKV_API int32_t pkv_allocator_num_cached(const pkv_allocator* a);
 
 /* Human-readable name of a status code (static string). */
 PKV_API const char* pkv_status_string(int status);

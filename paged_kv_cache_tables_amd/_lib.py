@@ -15,7 +15,7 @@ _LIB_NAME = "libpagedkv.so"
 _lib = None
 
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape", -3: "workspace too small",
-          -4: "HIP launch error"}
+          -4: "HIP launch error", -5: "no free blocks"}
 
 
 class PagedKVError(RuntimeError):
@@ -58,6 +58,32 @@ def load_library() -> ctypes.CDLL:
                                         c_void_p, c_int32, c_int64, c_int32, c_int32, c_int32, c_int32,
                                         c_int32, c_int64, c_int32, c_float, c_float, c_float, c_void_p,
                                         c_size_p, c_void_p]
+    lib.kv_copy_blocks.restype = c_int
+    lib.kv_copy_blocks.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int64, c_int32, c_int32,
+                                   c_int32, c_int32, c_void_p]
+    i32p, i64p = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    lib.pkv_allocator_create.restype = c_void_p
+    lib.pkv_allocator_create.argtypes = [c_int32, c_int32]
+    lib.pkv_allocator_destroy.restype = None
+    lib.pkv_allocator_destroy.argtypes = [c_void_p]
+    lib.pkv_allocator_allocate.restype = c_int
+    lib.pkv_allocator_allocate.argtypes = [c_void_p, i32p, c_int32, c_int32, i64p, i32p, c_int32, i32p, i32p]
+    lib.pkv_allocator_free.restype = c_int
+    lib.pkv_allocator_free.argtypes = [c_void_p, c_int64, i32p, c_int32]
+    lib.pkv_allocator_fork.restype = c_int
+    lib.pkv_allocator_fork.argtypes = [c_void_p, c_int64, c_int32, i64p, i32p, c_int32, i32p]
+    lib.pkv_allocator_extend.restype = c_int
+    lib.pkv_allocator_extend.argtypes = [c_void_p, c_int64, c_int32, i32p, c_int32, i32p]
+    lib.pkv_allocator_prepare_write.restype = c_int
+    lib.pkv_allocator_prepare_write.argtypes = [c_void_p, c_int64, c_int32, i32p, i32p]
+    lib.pkv_allocator_slots.restype = c_int
+    lib.pkv_allocator_slots.argtypes = [c_void_p, c_int64, c_int32, c_int32, i64p]
+    lib.pkv_allocator_table.restype = c_int
+    lib.pkv_allocator_table.argtypes = [c_void_p, c_int64, i32p, c_int32, i32p]
+    lib.pkv_allocator_num_free.restype = c_int32
+    lib.pkv_allocator_num_free.argtypes = [c_void_p]
+    lib.pkv_allocator_num_cached.restype = c_int32
+    lib.pkv_allocator_num_cached.argtypes = [c_void_p]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_status_string.argtypes = [c_int]
     _lib = lib
@@ -245,3 +271,138 @@ def paged_attention_fp8(out, q, k_cache, v_cache, block_tables, seq_lens, query_
                                  _stream_ptr(stream, dev))
     if st != 0:
         raise PagedKVError("paged_attention_fp8", st)
+
+
+def kv_copy_blocks(k_cache, v_cache, src, dst, stream=None) -> None:
+    """Copy whole blocks src[i] -> dst[i] (int32 device tensors) in both pools (bf16 or uint8)."""
+    import torch
+    dev = k_cache.device
+    if k_cache.dtype == torch.float8_e4m3fn:
+        k_cache, v_cache = k_cache.view(torch.uint8), v_cache.view(torch.uint8)
+    if k_cache.dtype not in (torch.bfloat16, torch.uint8) or v_cache.dtype != k_cache.dtype:
+        raise TypeError("pools must both be bf16 or both uint8")
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _check(t, n, k_cache.dtype, 4, dev)
+    for t, n in ((src, "src"), (dst, "dst")):
+        _check(t, n, torch.int32, 1, dev)
+    if src.shape != dst.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("src/dst or pool shapes differ")
+    NB, bs, Hkv, D = k_cache.shape
+    st = load_library().kv_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), src.data_ptr(), dst.data_ptr(),
+                                       src.shape[0], NB, bs, Hkv, D, k_cache.element_size(),
+                                       _stream_ptr(stream, dev))
+    if st != 0:
+        raise PagedKVError("kv_copy_blocks", st)
+
+
+class AllocatorFull(RuntimeError):
+    """No free blocks for the request, even after evicting every unreferenced cached prefix."""
+
+
+class BlockAllocator:
+    """The library's host block allocator with a radix prefix cache (pkv_allocator_*).
+
+    allocate(tokens, n_total) -> (id, blocks, cached prefix length); free(id, tokens);
+    fork(id, n_tokens) -> (id, blocks); extend(id, n_total) -> blocks;
+    prepare_write(id, pos) -> None or (src, dst); slots(id, start, count); table(id).
+    ``error``: the exception class raised when blocks run out (default AllocatorFull)."""
+
+    def __init__(self, num_blocks: int, block_size: int, error=AllocatorFull):
+        self._lib = load_library()
+        h = self._lib.pkv_allocator_create(int(num_blocks), int(block_size))
+        if not h:
+            raise ValueError("num_blocks >= 2 and block_size >= 1 are required")
+        self._h = ctypes.c_void_p(h)
+        self.num_blocks, self.block_size, self._error = int(num_blocks), int(block_size), error
+        self._cap = {}
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and self._lib is not None:
+            self._lib.pkv_allocator_destroy(h)
+            self._h = None
+
+    def _status(self, st, what, key=None):
+        if st == -5:
+            raise self._error(f"{what}: no free blocks")
+        if st != 0:
+            if key is not None and key not in self._cap:
+                raise KeyError(key)
+            raise ValueError(f"{what}: {STATUS.get(st, st)}")
+
+    @staticmethod
+    def _i32(seq):
+        """int32 token ids as a C pointer (a contiguous int32 numpy array is passed as is)."""
+        import numpy as np
+        arr = np.ascontiguousarray(seq, dtype=np.int32)
+        if arr.size == 0:
+            arr = np.zeros(1, dtype=np.int32)
+        return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+    def allocate(self, tokens, n_total: int):
+        keep, toks = self._i32(tokens)
+        cap = max(1, -(-int(n_total) // self.block_size))
+        out = (ctypes.c_int32 * cap)()
+        aid, nb, pre = ctypes.c_int64(0), ctypes.c_int32(0), ctypes.c_int32(0)
+        st = self._lib.pkv_allocator_allocate(self._h, toks, len(tokens), int(n_total), ctypes.byref(aid), out, cap,
+                                              ctypes.byref(nb), ctypes.byref(pre))
+        self._status(st, "allocate")
+        self._cap[aid.value] = nb.value
+        return aid.value, list(out[:nb.value]), pre.value
+
+    def free(self, alloc_id: int, tokens) -> None:
+        keep, toks = self._i32(tokens)
+        st = self._lib.pkv_allocator_free(self._h, int(alloc_id), toks, len(tokens))
+        self._status(st, "free", alloc_id)
+        del self._cap[alloc_id]
+
+    def table(self, alloc_id: int):
+        n = ctypes.c_int32(0)
+        st = self._lib.pkv_allocator_table(self._h, int(alloc_id), None, 0, ctypes.byref(n))
+        self._status(st, "table", alloc_id)
+        out = (ctypes.c_int32 * max(1, n.value))()
+        st = self._lib.pkv_allocator_table(self._h, int(alloc_id), out, n.value, ctypes.byref(n))
+        self._status(st, "table", alloc_id)
+        return list(out[:n.value])
+
+    def fork(self, alloc_id: int, n_tokens: int):
+        if alloc_id not in self._cap:
+            raise KeyError(alloc_id)
+        cap = max(1, self._cap[alloc_id])
+        out = (ctypes.c_int32 * cap)()
+        nid, nb = ctypes.c_int64(0), ctypes.c_int32(0)
+        st = self._lib.pkv_allocator_fork(self._h, int(alloc_id), int(n_tokens), ctypes.byref(nid), out, cap,
+                                          ctypes.byref(nb))
+        self._status(st, "fork", alloc_id)
+        self._cap[nid.value] = nb.value
+        return nid.value, list(out[:nb.value])
+
+    def extend(self, alloc_id: int, n_total: int):
+        if alloc_id not in self._cap:
+            raise KeyError(alloc_id)
+        cap = max(self._cap[alloc_id], -(-int(n_total) // self.block_size), 1)
+        out = (ctypes.c_int32 * cap)()
+        nb = ctypes.c_int32(0)
+        st = self._lib.pkv_allocator_extend(self._h, int(alloc_id), int(n_total), out, cap, ctypes.byref(nb))
+        self._status(st, "extend", alloc_id)
+        self._cap[alloc_id] = nb.value
+        return list(out[:nb.value])
+
+    def prepare_write(self, alloc_id: int, pos: int):
+        src, dst = ctypes.c_int32(-1), ctypes.c_int32(-1)
+        st = self._lib.pkv_allocator_prepare_write(self._h, int(alloc_id), int(pos), ctypes.byref(src),
+                                                   ctypes.byref(dst))
+        self._status(st, "prepare_write", alloc_id)
+        return None if src.value < 0 else (src.value, dst.value)
+
+    def slots(self, alloc_id: int, start: int, count: int):
+        out = (ctypes.c_int64 * max(1, int(count)))()
+        st = self._lib.pkv_allocator_slots(self._h, int(alloc_id), int(start), int(count), out)
+        self._status(st, "slots", alloc_id)
+        return list(out[:int(count)])
+
+    def num_free(self) -> int:
+        return int(self._lib.pkv_allocator_num_free(self._h))
+
+    def num_cached(self) -> int:
+        return int(self._lib.pkv_allocator_num_cached(self._h))

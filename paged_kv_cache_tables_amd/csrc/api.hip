@@ -96,6 +96,7 @@ const char* pkv_status_string(int status) {
     case PKV_EUNSUPPORTED: return "unsupported shape";
     case PKV_EWORKSPACE: return "workspace too small";
     case PKV_EHIP: return "HIP launch error";
+    case PKV_ENOSPACE: return "no free blocks";
   }
   return "unknown status";
 }
@@ -115,6 +116,22 @@ int kv_append(const void* k_new, const void* v_new, const int64_t* slot_mapping,
   const int row_chunks = num_kv_heads * head_dim / 8;
   hipError_t e = pkv::launch_append(k_new, v_new, slot_mapping, num_tokens, k_cache, v_cache,
                                     num_blocks * block_size, row_chunks, (hipStream_t)stream);
+  return e == hipSuccess ? PKV_OK : PKV_EHIP;
+}
+
+int kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst, int32_t n_pairs,
+                   int64_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t elem_bytes, void* stream) {
+  if (n_pairs < 0 || num_blocks <= 0 || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      (elem_bytes != 1 && elem_bytes != 2))
+    return PKV_EINVAL;
+  const int64_t block_bytes = (int64_t)block_size * num_kv_heads * head_dim * elem_bytes;
+  if (block_bytes % 16 != 0) return PKV_EUNSUPPORTED;
+  if (n_pairs == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !src || !dst) return PKV_EINVAL;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(src, 4) || !aligned(dst, 4)) return PKV_EINVAL;
+  hipError_t e = pkv::launch_copy_blocks(k_cache, v_cache, src, dst, n_pairs, num_blocks, block_bytes / 16,
+                                         (hipStream_t)stream);
   return e == hipSuccess ? PKV_OK : PKV_EHIP;
 }
 

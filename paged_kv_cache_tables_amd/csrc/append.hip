@@ -48,6 +48,31 @@ hipError_t launch_append(const void* k_new, const void* v_new, const int64_t* sl
   return hipGetLastError();
 }
 
+// ---- whole-block copies (copy-on-write of a shared block) ----
+// Workgroup i copies pair i's block in K and in V, 16 bytes per thread and step.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint4* __restrict__ k_cache, uint4* __restrict__ v_cache,
+                                                          const int32_t* __restrict__ src,
+                                                          const int32_t* __restrict__ dst, int64_t num_blocks,
+                                                          int64_t chunks16) {
+  const int32_t s = src[blockIdx.x], d = dst[blockIdx.x];
+  if (s == d || s < 0 || d < 0 || s >= num_blocks || d >= num_blocks) return;
+  const uint4* ks = k_cache + (int64_t)s * chunks16;
+  const uint4* vs = v_cache + (int64_t)s * chunks16;
+  uint4* kd = k_cache + (int64_t)d * chunks16;
+  uint4* vd = v_cache + (int64_t)d * chunks16;
+  for (int64_t c = threadIdx.x; c < chunks16; c += blockDim.x) {
+    kd[c] = ks[c];
+    vd[c] = vs[c];
+  }
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst, int n_pairs,
+                              int64_t num_blocks, int64_t chunks16, hipStream_t stream) {
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)n_pairs), dim3(256), 0, stream, (uint4*)k_cache,
+                     (uint4*)v_cache, src, dst, num_blocks, chunks16);
+  return hipGetLastError();
+}
+
 // ---- E4M3 pools ----
 //
 // An 8-bit cache stores, for each value x of a new row, the E4M3 code nearest to

@@ -49,6 +49,11 @@ hipError_t launch_append_fp8(const void* k_new, const void* v_new, const int64_t
                              void* k_cache, void* v_cache, int64_t num_slots, int row_chunks16,
                              float k_scale, float v_scale, hipStream_t stream);
 
+// Whole-block copies of both pools: pair i copies block src[i] to dst[i] (chunks16 = 16-byte
+// chunks per block).
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst, int n_pairs,
+                              int64_t num_blocks, int64_t chunks16, hipStream_t stream);
+
 // fp8: the pools hold E4M3 codes instead of bf16.
 bool decode_supported(int D, int G, int bs, bool fp8);
 hipError_t launch_decode(const AttnParams& p, bool fp8, hipStream_t stream);
