@@ -217,6 +217,9 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
   if (fp8) p.scale_log2 *= k_scale;               // scores of codes, times the K scale
   p.v_scale = fp8 ? v_scale : 1.f;
   p.decode_waves = decode_waves_for_current_device();
+  // the KV heads a decode workgroup reads together: the largest power of two <= 8 dividing Hkv
+  p.decode_group = 1;
+  while (p.decode_group < pkv::kMaxDecodeGroup && num_kv_heads % (2 * p.decode_group) == 0) p.decode_group *= 2;
   p.decode_max_q = decode_rows(num_q_heads, num_kv_heads, max_query_len);
   p.min_share_tiles = kMinShareTokens / 64;
   p.max_splits = ws.max_splits;

@@ -84,7 +84,7 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // every E4M3 value is a bf16 value) on their way into LDS, the K pool scale is folded
 // into the score scale and the V pool scale into the output.
 template <int D, int G, int BS, bool MULTI, bool F8>
-__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2, 8)))
+__global__ __launch_bounds__(kMaxDecodeGroup * kWave) __attribute__((amdgpu_waves_per_eu(2, 8)))
 void decode_kernel(AttnParams p) {
   constexpr int CH = D / 8;              // 16-byte bf16 chunks per row in LDS
   constexpr int EB = F8 ? 1 : 2;         // bytes per pool value
@@ -98,15 +98,21 @@ void decode_kernel(AttnParams p) {
   static_assert(G <= 16, "a GQA group is one 16-column MFMA tile");
   static_assert(kTile % BS == 0 && BS % RPI == 0, "a wave-wide load stays inside one pool block");
 
-  __shared__ __attribute__((aligned(16))) uint4 tile[kTile][CH];   // K, then V, of the current tile
-
-  const int lane = threadIdx.x;
-  const int w = blockIdx.x;
+  // one [kTile][CH] tile per wave: K, then V, of the wave's current tile
+  extern __shared__ __attribute__((aligned(16))) uint4 lds_tiles[];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = uniform((int)(threadIdx.x / kWave));   // wave of the workgroup = KV head within the group
+  uint4 (*tile)[CH] = reinterpret_cast<uint4 (*)[CH]>(lds_tiles + (size_t)wv * kTile * CH);
+  const int w = blockIdx.x;                      // workgroup = one share of the units
   const int Hkv = p.Hkv;
+  const int WPG = p.decode_group;                // KV heads (waves) per workgroup; divides Hkv
+  const int NG = Hkv / WPG;                      // head groups
 
-  // ---- the partition: units (s, h, tile) in that order, an equal share per wave ----
-  // Lane l sums the tiles of sequences [l c, (l + 1) c); a wave scan gives each lane the
-  // units before its chunk.  Unit counts fit in 32 bits (checked by the host).
+  // ---- the partition: units (s, head group, tile) in that order, an equal share per workgroup ----
+  // The waves of a workgroup take the same units for the heads of one group, so the heads'
+  // rows of each pool slot (adjacent in memory) are read at the same time.  Lane l sums the
+  // tiles of sequences [l c, (l + 1) c); a wave scan gives each lane the units before its
+  // chunk.  Unit counts fit in 32 bits (checked by the host).
   const int c_per = (p.num_seqs + kWave - 1) / kWave;
   int my_tiles = 0;
   SeqInfo first{0, 0, 0, 0};                     // this lane's first sequence
@@ -119,15 +125,16 @@ void decode_kernel(AttnParams p) {
     }
   }
   const int incl = wave_incl_scan(my_tiles);
-  const int total_units = uniform(__shfl(incl, kWave - 1, kWave) * Hkv);
+  const int total_units = uniform(__shfl(incl, kWave - 1, kWave) * NG);
   if (total_units == 0) return;
-  const int share = uniform(max(p.min_share_tiles, (total_units + p.decode_waves - 1) / p.decode_waves));
-  if (w >= (total_units + share - 1) / share) return;   // fewer shares than waves
+  const int nwg = p.decode_waves / WPG;          // workgroups of the grid
+  const int share = uniform(max(p.min_share_tiles, (total_units + nwg - 1) / nwg));
+  if (w >= (total_units + share - 1) / share) return;   // fewer shares than workgroups
   const int x0 = w * share;
   const int x1 = min(x0 + share, total_units);
   // the lane whose chunk holds unit x0, then the sequence inside that chunk
-  const int excl_units = (incl - my_tiles) * Hkv;
-  const unsigned long long hit = __builtin_amdgcn_ballot_w64(excl_units <= x0 && x0 < incl * Hkv);
+  const int excl_units = (incl - my_tiles) * NG;
+  const unsigned long long hit = __builtin_amdgcn_ballot_w64(excl_units <= x0 && x0 < incl * NG);
   const int src = (int)__builtin_ctzll(hit);     // nonempty: x0 < total_units
   int s = uniform(src * c_per);
   int seg_a = uniform(__shfl(excl_units, src, kWave));   // first unit of sequence s
@@ -136,7 +143,7 @@ void decode_kernel(AttnParams p) {
   int cur_len = uniform(__shfl(first.len, src, kWave));
   int nt = uniform(__shfl(first.tiles, src, kWave));
   auto next_seq = [&]() {
-    seg_a += Hkv * nt;
+    seg_a += NG * nt;
     s = uniform(s + 1);
     const SeqInfo si = seq_info(p, s);
     cur_row0 = uniform(si.row0);
@@ -144,7 +151,7 @@ void decode_kernel(AttnParams p) {
     cur_len = uniform(si.len);
     nt = uniform(si.tiles);
   };
-  while (x0 >= seg_a + Hkv * nt && s + 1 < p.num_seqs) next_seq();
+  while (x0 >= seg_a + NG * nt && s + 1 < p.num_seqs) next_seq();
 
   const int n = lane & 15;                       // accumulator column: query head of the group
   const int kg = lane >> 4;                      // k-group / accumulator row group
@@ -366,19 +373,20 @@ void decode_kernel(AttnParams p) {
     }
   };
 
-  // ---- walk the share: pieces of consecutive (s, h) segments ----
+  // ---- walk the share: pieces of consecutive (s, head group) segments; this wave takes
+  // the head wv of each group ----
   int pos = x0;
   while (pos < x1) {
-    if (pos >= seg_a + Hkv * nt) {               // past sequence s: next sequence with decode tiles
+    if (pos >= seg_a + NG * nt) {                // past sequence s: next sequence with decode tiles
       if (s + 1 >= p.num_seqs) break;            // not reached: pos < total_units
       next_seq();
       continue;
     }
-    const int h = (pos - seg_a) / nt;
-    const int a = seg_a + h * nt;                // first unit of (s, h)
+    const int hg = (pos - seg_a) / nt;
+    const int a = seg_a + hg * nt;               // first unit of (s, hg)
     const int tb0 = pos - a;
     const int tb1 = min(x1, a + nt) - a;
-    piece(h, tb0, tb1, a);
+    piece(hg * WPG + wv, tb0, tb1, a);
     pos = a + tb1;
   }
 }
@@ -456,10 +464,12 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(AttnParams p
 
 template <int D, int G, int BS, bool F8>
 hipError_t launch_decode_t(const AttnParams& p, hipStream_t stream) {
+  const dim3 grid(p.decode_waves / p.decode_group), block(p.decode_group * kWave);
+  const size_t lds = (size_t)p.decode_group * kTile * (D / 8) * 16;   // one bf16 tile per wave
   if (p.decode_max_q > 1)
-    hipLaunchKernelGGL((decode_kernel<D, G, BS, true, F8>), dim3(p.decode_waves), dim3(kWave), 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<D, G, BS, true, F8>), grid, block, lds, stream, p);
   else
-    hipLaunchKernelGGL((decode_kernel<D, G, BS, false, F8>), dim3(p.decode_waves), dim3(kWave), 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<D, G, BS, false, F8>), grid, block, lds, stream, p);
   return hipGetLastError();
 }
 

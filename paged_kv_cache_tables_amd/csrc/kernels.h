@@ -25,6 +25,7 @@ struct AttnParams {
                                   // scores live in the exp2 domain
   float v_scale;                  // E4M3 pools: the V pool scale, applied to the output (1 for bf16)
   int decode_waves;               // decode grid: one wave per resident wave slot of the device
+  int decode_group;               // decode waves per workgroup: the KV heads taken together (divides Hkv)
   int decode_max_q;               // sequences with 1 <= q_s <= this are decode rows (q_s x G <= 16)
   int min_share_tiles;            // smallest share of 64-token tiles a decode wave takes
   int max_splits;                 // pieces one (sequence, head) can be cut into: bounds the partials
@@ -37,6 +38,9 @@ struct AttnParams {
   int plan_capacity;              // items the workspace holds
   int plan_stride;                // host bound on the items of this call (grid = Hkv * stride)
 };
+
+// Most KV heads (waves) one decode workgroup takes together.
+constexpr int kMaxDecodeGroup = 8;
 
 // Query rows packed into one prefill workgroup (with all G heads of each row).
 constexpr int kPrefillPairs = 128;

@@ -274,6 +274,32 @@ def test_caller_workspace_and_stream(gpu):
         db.attend(workspace=ws[: need - 256])
 
 
+def test_one_workspace_serves_calls_of_any_shape(gpu):
+    """A workspace needs no initialisation and carries nothing between calls: one buffer,
+    filled with junk before every call, serves calls of changing shape in turn."""
+    torch = gpu
+    import paged_kv_cache_tables_amd as pkv
+    cases = [W.custom("ws-many", [(1 + (i * 53) % 3000, 1) for i in range(200)], 32, 8, 128, 16, seed=11),
+             W.custom("ws-long", [(60000, 1), (5000, 1)], 16, 2, 128, 16, seed=12),
+             W.custom("ws-multi", [(2000, 4), (700, 2), (300, 30)], 16, 4, 128, 16, seed=13),
+             W.config1(num_seqs=16)]
+    need = max(pkv.workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                   wl.max_blocks_per_seq, wl.block_size, wl.max_query_len) for wl in cases)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    for rnd in range(2):
+        for wl in cases:
+            print(f"shared workspace: {wl.name} round {rnd}", flush=True)
+            db = DeviceBatch(wl)
+            db.append()
+            ws.fill_(0x5A + rnd)
+            db.attend(workspace=ws)
+            torch.cuda.synchronize()
+            k2, v2 = oracle_after_append(wl)
+            ref = oracle.paged_attention(wl.q, k2, v2, wl.block_tables, wl.seq_lens, wl.query_start_loc,
+                                         wl.num_kv_heads, wl.scale)
+            compare(to_host_bits(db.out), ref, label=f"shared-ws-{wl.name}")
+
+
 @pytest.mark.parametrize("cfg", [0, 1])
 def test_step_captured_in_hip_graph(gpu, cfg):
     """append + attention captured once in a HIP graph (the library allocates, memsets and
