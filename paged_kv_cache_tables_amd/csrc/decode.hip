@@ -1,12 +1,13 @@
-// Decode rows (one query token per sequence): split-K paged attention plus a
-// log-sum-exp merge of the splits.
+// Decode rows (one query token per sequence, or a few for short chunks such as
+// speculative verification): split-K paged attention plus a log-sum-exp merge of
+// the pieces.
 //
 // What is computed is the exact softmax attention of "Under the Hood: Flash
 // Attention" (Text Generation Inference page): a running max m, a running sum
 // l of exponentials and an output accumulator rescaled by exp(m_old - m_new)
 // whenever the max grows, finished by O / l.  The same rescale identity
 // merges partial (O, m, l) triples computed over disjoint key ranges, which is
-// what the merge kernel does across splits.  Keys and values are reached
+// what the merge kernel does across pieces.  Keys and values are reached
 // through the sequence's block table ("Under the Hood: PagedAttention").
 //
 // Why matrix cores for a bandwidth-bound step: with a GQA group of G query
@@ -18,10 +19,14 @@
 // dense contractions ([G x D] x [D x T]), so they run on bf16 MFMA with fp32
 // accumulation and the vector ALUs are left with the softmax.
 //
-// Layout (gfx950, one 64-lane wave per workgroup, v_mfma_f32_16x16x32_bf16):
-//   grid = (kv head, split, sequence), KV heads fastest: the heads of one split
-//   read the same pool rows (heads are interleaved in a slot) close in time.
-//   The wave walks the split's 64-token tiles.
+// Layout (gfx950, v_mfma_f32_16x16x32_bf16):
+//   * Partition: the decode rows' work is cut into units (sequence, group of
+//     KV heads, 64-token tile), in that order.  The grid has one wave per
+//     resident wave slot of the device; a workgroup holds one wave per KV head
+//     of a group (up to 8) and takes an equal consecutive share of units,
+//     walked as pieces of consecutive (sequence, group) segments.  The waves of a workgroup read the same slots for different
+//     heads, and a slot's heads sit side by side in the pool, so the DRAM rows
+//     behind each slot are read together.
 //   * Loads are fully coalesced: 16 lanes read one 256-byte row (16 bytes each),
 //     4 rows per instruction; the pool block of each instruction is
 //     wave-uniform (scalar base).  K and V of a tile arrive in registers.
@@ -37,8 +42,8 @@
 //     rounded to bf16 in place; A = V^T.
 //   * Streaming: each register set is refilled with the next tile as soon as
 //     its contents are in LDS, so K and V both run one tile ahead.
-//   A sequence with one split writes bf16 output directly, otherwise fp32
-//   partials (O, m, l) go to the workspace for the merge kernel.
+//   A piece that covers its whole (sequence, head) writes bf16 output directly;
+//   otherwise fp32 partials (O, m, l) go to the workspace for the merge kernel.
 #include "common.h"
 #include "kernels.h"
 
@@ -344,7 +349,7 @@ void decode_kernel(AttnParams p) {
     int n_e = n, kg_e = kg;
     asm volatile("" : "+v"(n_e), "+v"(kg_e));
     const int rr_e = n_e / G, g_e = n_e % G;
-    const int first_w = a / share;                 // the wave holding tile 0 of (s, h)
+    const int first_w = a / share;                 // the workgroup holding tile 0 of (s, h)
     const int nseg = (a + nt - 1) / share - first_w + 1;   // pieces of (s, h)
     if (tb0 == 0 && lane == 0) p.ws_nparts[(size_t)s * Hkv + h] = nseg;
     float l_tot = l_part + __shfl_xor(l_part, 16, kWave);
