@@ -1,8 +1,10 @@
 """Benchmark of the paged attention path on one MI355X.
 
-A step = kv_append of the batch's new tokens + one paged_attention call over
-the batch (every row of the hot path), on seeded synthetic inputs already
-resident in HBM.  Default workload: the Llama-3-8B-shaped decode layer (64
+A step = the append of the batch's new tokens + attention over the batch (every
+row of the hot path), on seeded synthetic inputs already resident in HBM: by
+default one paged_attention_append call (the append fused into the attention
+call), with --step separate kv_append then paged_attention (the 8-bit cache
+always uses its two calls).  Default workload: the Llama-3-8B-shaped decode layer (64
 sequences, contexts U{128..4096}, 32 query / 8 KV heads, d 128, 16-token
 blocks).  Several device copies of the batch are cycled so consecutive steps
 do not re-read the same lines from the 256 MB last-level cache.
@@ -10,9 +12,9 @@ do not re-read the same lines from the 256 MB last-level cache.
 Prints ONE JSON line on stdout:
   value         KV-read GB/s of the whole step: algorithmic K+V bytes (every
                 cached token of every sequence read once) / step time;
-  roofline      the attention call (split-K decode + merge), timed with HIP
-                events on its stream around every call of the timed region,
-                against the 8 TB/s HBM peak; `traffic` comes from rocprofv3
+  roofline      the attention call (fused append + split-K decode + merge),
+                timed with HIP events on its stream around every call of the
+                timed region, against the 8 TB/s HBM peak; `traffic` comes from rocprofv3
                 FETCH_SIZE/WRITE_SIZE counters stored under profiles/ (null if
                 the kernels changed since);
   call_us       median / p10 / p90 of those per-call times, and the median
@@ -21,6 +23,7 @@ Prints ONE JSON line on stdout:
                 mixed batch (8 chunks of 512 rows over prefixes of 0..2048
                 tokens, 32/8 heads, d 128) in a call of their own, TFLOP/s of
                 causal pairs against the 2.5 PFLOP/s bf16 peak;
+  separate_calls the same steps through kv_append + paged_attention;
   mixed         (mixed batch only) decode-only and prefill-only sub-batch times;
   append        kv_append alone at T = 64, 4288 and 65536 tokens (HBM GB/s);
   measured_peaks a device copy and a bf16 GEMM through torch, for context;
@@ -175,33 +178,48 @@ def time_calls(fn, n, warm, stream, torch):
     return [a.elapsed_time(b) for a, b in evs]
 
 
+def region_ms(fn, n, warm, stream, torch):
+    """Average ms of n back-to-back calls of fn, from one HIP event pair around all of them on
+    `stream` (no event between calls: each costs the stream idle time of its own)."""
+    for _ in range(warm):
+        fn()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(n):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
 def sub_attention_ms(pkv, d, sub, scale, stream, torch, n=20):
-    """Per-call times of paged_attention over a sub-batch (its own output and workspace)."""
+    """paged_attention over a sub-batch (its own output and workspace): (per-call times with an
+    event pair around each call, average over n back-to-back calls)."""
     wl = d.wl
     out = torch.empty_like(sub["q"])
     ws = torch.empty(pkv.workspace_bytes(sub["num_seqs"], wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
                                          wl.max_blocks_per_seq, wl.block_size, max(1, sub["max_query_len"])),
                      dtype=torch.uint8, device=d.dev)
-
-    def call():
-        pkv.paged_attention(out, sub["q"], d.t["kc"], d.t["vc"], sub["bt"], sub["sl"], sub["qsl"], scale,
-                            sub["max_query_len"], workspace=ws, stream=stream)
-    return time_calls(call, n, 3, stream, torch)
+    call = pkv.paged_attention(out, sub["q"], d.t["kc"], d.t["vc"], sub["bt"], sub["sl"], sub["qsl"], scale,
+                               sub["max_query_len"], workspace=ws, stream=stream, prepare=True)
+    return time_calls(call, n, 3, stream, torch), region_ms(call, n, 2, stream, torch)
 
 
 def prefill_report(pkv, d, stream, torch):
     wl = d.wl
     pre = wl.prefill_seqs()
     flops = 4 * wl.head_dim * wl.num_q_heads * wl.causal_pairs(pre)
-    ms = sub_attention_ms(pkv, d, d.subset(pre), wl.scale, stream, torch)
-    med = pct(ms, 50)
-    tf = flops / (med * 1e-3) / 1e12
+    ms, avg = sub_attention_ms(pkv, d, d.subset(pre), wl.scale, stream, torch)
+    tf = flops / (avg * 1e-3) / 1e12
     return {"workload": f"prefill rows of {wl.name}: {len(pre)} chunks, {int(wl.query_lens[pre].sum())} rows, "
                         f"prefixes {sorted(int(wl.seq_lens[s] - wl.query_lens[s]) for s in pre)}",
-            "flops_per_call": flops, "call_us_median": round(med * 1e3, 3),
+            "flops_per_call": flops, "call_us_avg": round(avg * 1e3, 3),
+            "call_us_median": round(pct(ms, 50) * 1e3, 3),
             "call_us_p10": round(pct(ms, 10) * 1e3, 3), "call_us_p90": round(pct(ms, 90) * 1e3, 3),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                         "timing": "HIP events around 20 back-to-back calls, / 20 (call_us_avg)",
                          "note": "flops = 4 d Hq x causal (row, key) pairs; the call also launches the "
                                  "(empty) decode and merge grids and the planner"}}
 
@@ -219,25 +237,24 @@ def append_report(pkv, dev, torch, stream):
         g = torch.Generator(device="cpu").manual_seed(T)
         slots = torch.randperm(nb * bs, generator=g)[:T].to(torch.int64).to(dev)
 
-        def call():
-            pkv.kv_append(kn, vn, slots, kc, vc, stream=stream)
+        call = pkv.kv_append(kn, vn, slots, kc, vc, stream=stream, prepare=True)
         ms = time_calls(call, 20, 3, stream, torch)
-        med = pct(ms, 50)
+        avg = region_ms(call, 20, 3, stream, torch)
         moved = 2 * 2 * T * Hkv * D * 2     # K and V, read once and written once
-        res[f"T{T}"] = {"us_median": round(med * 1e3, 3), "GBps": round(moved / (med * 1e-3) / 1e9, 1)}
-        del kc, vc, kn, vn, slots
+        res[f"T{T}"] = {"us_avg": round(avg * 1e3, 3), "us_median_with_events": round(pct(ms, 50) * 1e3, 3),
+                        "GBps": round(moved / (avg * 1e-3) / 1e9, 1)}
+        del kc, vc, kn, vn, slots, call
     return res
 
 
 def graph_report(pkv, c, wl, torch, n=30):
-    """One step (append + attention) captured in a HIP graph and replayed: the per-step
-    time without the Python and launch overhead of the eager calls."""
+    """One step (the fused append + attention call) captured in a HIP graph and replayed: the
+    per-step time without the Python and launch overhead of the eager call."""
     t = c.t
 
     def body():
-        pkv.kv_append(t["k_new"], t["v_new"], t["slots"], t["kc"], t["vc"])
-        pkv.paged_attention(t["out"], t["q"], t["kc"], t["vc"], t["bt"], t["sl"], t["qsl"], wl.scale,
-                            wl.max_query_len, workspace=t["ws"])
+        pkv.paged_attention_append(t["out"], t["q"], t["k_new"], t["v_new"], t["slots"], t["kc"], t["vc"],
+                                   t["bt"], t["sl"], t["qsl"], wl.scale, wl.max_query_len, workspace=t["ws"])
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -251,10 +268,11 @@ def graph_report(pkv, c, wl, torch, n=30):
     torch.cuda.synchronize()
     cur = torch.cuda.current_stream()
     ms = time_calls(g.replay, n, 3, cur, torch)
+    avg = region_ms(g.replay, n, 3, cur, torch)
     torch.cuda.synchronize()
     del g
-    return {"graph_step_us_median": round(pct(ms, 50) * 1e3, 3), "graph_step_us_p10": round(pct(ms, 10) * 1e3, 3),
-            "replays": n}
+    return {"graph_step_us_avg": round(avg * 1e3, 3), "graph_step_us_median": round(pct(ms, 50) * 1e3, 3),
+            "graph_step_us_p10": round(pct(ms, 10) * 1e3, 3), "replays": n}
 
 
 def fp8_report(pkv, d, torch, stream, bf16_call_us, n=30, copies=3):
@@ -275,14 +293,15 @@ def fp8_report(pkv, d, torch, stream, bf16_call_us, n=30, copies=3):
                                          wl.max_blocks_per_seq, wl.block_size, wl.max_query_len),
                      dtype=torch.uint8, device=d.dev)
     it = [0]
+    calls = [pkv.paged_attention_fp8(out, t["q"], kc, vc, t["bt"], t["sl"], t["qsl"], wl.scale, wl.max_query_len,
+                                     f8.k_scale, f8.v_scale, workspace=ws, stream=stream, prepare=True)
+             for kc, vc in pools]
 
     def call():
-        kc, vc = pools[it[0] % copies]
+        calls[it[0] % copies]()
         it[0] += 1
-        pkv.paged_attention_fp8(out, t["q"], kc, vc, t["bt"], t["sl"], t["qsl"], wl.scale, wl.max_query_len,
-                                f8.k_scale, f8.v_scale, workspace=ws, stream=stream)
     ms = time_calls(call, n, 3, stream, torch)
-    med = pct(ms, 50)
+    med = region_ms(call, n, 3, stream, torch)
     code_bytes = wl.kv_read_bytes() // 2
     uniq = wl.unique_kv_read_bytes() // 2
     # the append of the step's new tokens alone
@@ -290,12 +309,12 @@ def fp8_report(pkv, d, torch, stream, bf16_call_us, n=30, copies=3):
     ams = time_calls(lambda: pkv.kv_append_fp8(t["k_new"], t["v_new"], t["slots"], kc, vc, f8.k_scale,
                                                f8.v_scale, stream=stream), 20, 3, stream, torch)
     res = {"workload": workload_desc(wl) + ", E4M3 pools (scales 2^-4, 2^-3)",
-           "kv_code_bytes_per_call": code_bytes, "call_us_median": round(med * 1e3, 3),
-           "call_us_p10": round(pct(ms, 10) * 1e3, 3),
+           "kv_code_bytes_per_call": code_bytes, "call_us_avg": round(med * 1e3, 3),
+           "call_us_median": round(pct(ms, 50) * 1e3, 3), "call_us_p10": round(pct(ms, 10) * 1e3, 3),
            "GBps": round(uniq / (med * 1e-3) / 1e9, 1), "frac_of_hbm_peak": round(uniq / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
            "speedup_vs_bf16_call": round(bf16_call_us / (med * 1e3), 3),
            "append_fp8_us_median": round(pct(ams, 50) * 1e3, 3)}
-    del pools, out, ws
+    del pools, out, ws, calls
     torch.cuda.empty_cache()
     return res
 
@@ -316,16 +335,15 @@ def prefill_fp8_report(pkv, d, torch, stream):
                                          wl.max_blocks_per_seq, wl.block_size, sub["max_query_len"]),
                      dtype=torch.uint8, device=d.dev)
 
-    def call():
-        pkv.paged_attention_fp8(out, sub["q"], kc, vc, sub["bt"], sub["sl"], sub["qsl"], wl.scale,
-                                sub["max_query_len"], f8.k_scale, f8.v_scale, workspace=ws, stream=stream)
-    ms = time_calls(call, 20, 3, stream, torch)
-    med = pct(ms, 50)
+    call = pkv.paged_attention_fp8(out, sub["q"], kc, vc, sub["bt"], sub["sl"], sub["qsl"], wl.scale,
+                                   sub["max_query_len"], f8.k_scale, f8.v_scale, workspace=ws, stream=stream,
+                                   prepare=True)
+    med = region_ms(call, 20, 3, stream, torch)
     flops = 4 * wl.head_dim * wl.num_q_heads * wl.causal_pairs(pre)
     tf = flops / (med * 1e-3) / 1e12
-    del kc, vc, out, ws
+    del kc, vc, out, ws, call
     torch.cuda.empty_cache()
-    return {"call_us_median": round(med * 1e3, 3), "TFLOPs": round(tf, 1), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+    return {"call_us_avg": round(med * 1e3, 3), "TFLOPs": round(tf, 1), "frac_of_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
 
 
 def allocator_report(pkv, n_rounds=5):
@@ -383,8 +401,8 @@ def measured_peaks(torch, dev, stream):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=1, help="workload: 0..4 (1 = Llama-3-8B decode)")
     ap.add_argument("--copies", type=int, default=3, help="device copies of the batch cycled per step")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
@@ -392,6 +410,8 @@ def main():
     ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
                     help="cache element type of the timed step: bf16 (default) or 8-bit E4M3 codes with "
                          "per-pool scales (kv_append_fp8 + paged_attention_fp8; implies --no-extras)")
+    ap.add_argument("--step", choices=["fused", "separate"], default="fused",
+                    help="timed step: paged_attention_append, or kv_append then paged_attention (bf16 cache)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the prefill, append and peak measurements (step timing and roofline only)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -443,50 +463,92 @@ def main():
         c.t["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def append(c):
+    # Each call is checked and marshalled once per device copy (PreparedCall), so the timed
+    # loop issues bare C calls: the host cost per step stays below the device time.
+    def prep_append(c):
         t = c.t
         if fp8:
-            pkv.kv_append_fp8(t["k_new"], t["v_new"], t["slots"], t["kc"], t["vc"], f8.k_scale, f8.v_scale,
-                              stream=stream)
-        else:
-            pkv.kv_append(t["k_new"], t["v_new"], t["slots"], t["kc"], t["vc"], stream=stream)
+            return pkv.kv_append_fp8(t["k_new"], t["v_new"], t["slots"], t["kc"], t["vc"], f8.k_scale, f8.v_scale,
+                                     stream=stream, prepare=True)
+        return pkv.kv_append(t["k_new"], t["v_new"], t["slots"], t["kc"], t["vc"], stream=stream, prepare=True)
+
+    def prep_fused(c):
+        t = c.t
+        return pkv.paged_attention_append(t["out"], t["q"], t["k_new"], t["v_new"], t["slots"], t["kc"], t["vc"],
+                                          t["bt"], t["sl"], t["qsl"], wl.scale, wl.max_query_len, workspace=t["ws"],
+                                          stream=stream, prepare=True)
+
+    def prep_attend(c):
+        t = c.t
+        if fp8:
+            return pkv.paged_attention_fp8(t["out"], t["q"], t["kc"], t["vc"], t["bt"], t["sl"], t["qsl"], wl.scale,
+                                           wl.max_query_len, f8.k_scale, f8.v_scale, workspace=t["ws"],
+                                           stream=stream, prepare=True)
+        return pkv.paged_attention(t["out"], t["q"], t["kc"], t["vc"], t["bt"], t["sl"], t["qsl"], wl.scale,
+                                   wl.max_query_len, workspace=t["ws"], stream=stream, prepare=True)
+
+    for c in copies:
+        c.append, c.attend = prep_append(c), prep_attend(c)
+        c.fused = None if fp8 else prep_fused(c)
+
+    def append(c):
+        c.append()
+
+    def fused_step(c):
+        c.fused()
 
     def attend(c):
-        t = c.t
-        if fp8:
-            pkv.paged_attention_fp8(t["out"], t["q"], t["kc"], t["vc"], t["bt"], t["sl"], t["qsl"], wl.scale,
-                                    wl.max_query_len, f8.k_scale, f8.v_scale, workspace=t["ws"], stream=stream)
-        else:
-            pkv.paged_attention(t["out"], t["q"], t["kc"], t["vc"], t["bt"], t["sl"], t["qsl"], wl.scale,
-                                wl.max_query_len, workspace=t["ws"], stream=stream)
+        c.attend()
 
-    for i in range(args.warmup):
-        append(copies[i % len(copies)])
-        attend(copies[i % len(copies)])
+    use_fused = args.step == "fused" and not fp8   # the 8-bit cache has no fused call
+
+    def run_steps(n, fused_call, evs=None):
+        for i in range(n):
+            c = copies[i % len(copies)]
+            if fused_call:
+                if evs is not None:
+                    evs[i][0].record(stream)
+                fused_step(c)
+            else:
+                append(c)
+                if evs is not None:
+                    evs[i][0].record(stream)
+                attend(c)
+            if evs is not None:
+                evs[i][1].record(stream)
+
+    run_steps(args.warmup, use_fused)
     torch.cuda.synchronize()
 
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    # Timed region: K steps back to back, one HIP event pair around the region on the
+    # library's stream (an event recorded between calls costs the stream ~5 us of idle
+    # time, so none is recorded inside the region).  With the fused step the region holds
+    # nothing but the K attention calls, so its event time / K is the call's duration.
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        c = copies[i % len(copies)]
-        append(c)
-        evs[i][0].record(stream)
-        attend(c)
-        evs[i][1].record(stream)
+    ev0.record(stream)
+    run_steps(args.steps, use_fused)
+    ev1.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    region_ms = ev0.elapsed_time(ev1)
 
     ms_per_step = elapsed * 1e3 / args.steps
+    attn_avg_ms = region_ms / args.steps
+    # spread of single calls: a second pass with an event pair around each call
+    n_spread = min(args.steps, 30)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_spread)]
+    run_steps(n_spread, use_fused, evs)
+    torch.cuda.synchronize()
     attn_ms = [a.elapsed_time(b) for a, b in evs]
-    attn_avg_ms = float(np.mean(attn_ms))
     kv_bytes = wl.kv_read_bytes() // (2 if fp8 else 1)          # one byte per value for E4M3 pools
     uniq_bytes = wl.unique_kv_read_bytes() // (2 if fp8 else 1)
     dec = wl.decode_seqs()
     pre = wl.prefill_seqs()
     value = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = uniq_bytes / (attn_avg_ms * 1e-3) / 1e9
-    hot_ms = time_calls(lambda: attend(copies[0]), 10, 2, stream, torch)
+    hot_ms = time_calls(lambda: (fused_step if use_fused else attend)(copies[0]), 10, 2, stream, torch)
 
     result = {
         "metric": METRIC,
@@ -507,36 +569,59 @@ def main():
                    "appended_tokens": wl.num_q_tokens, "device_copies_cycled": len(copies),
                    "kv_cache": "e4m3, per-pool scales 2^-4 (K), 2^-3 (V)" if fp8 else "bf16"},
         "decode_tokens_per_s": round(len(dec) / (ms_per_step * 1e-3), 1),
-        "roofline": {"bound": "hbm", "kernel": ("paged_attention_fp8" if fp8 else "paged_attention")
-                     + " call (split-K decode + LSE merge"
-                     + (" + prefill" if len(pre) else "") + ")",
+        "step": ("paged_attention_append (kv_append fused into the attention call)" if use_fused
+                 else "kv_append_fp8 + paged_attention_fp8" if fp8 else "kv_append + paged_attention"),
+        "roofline": {"bound": "hbm", "kernel": ("paged_attention_append call (append + " if use_fused else
+                                                "kv_append_fp8 + paged_attention_fp8 step (" if fp8 else
+                                                "kv_append + paged_attention step (")
+                     + "split-K decode + LSE merge" + (" + prefill" if len(pre) else "") + ")",
+                     "timing": "HIP events around the timed region on the library's stream, / steps",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "avg_call_us": round(attn_avg_ms * 1e3, 3),
                      "algorithmic_bytes_per_call": uniq_bytes,
-                     "traffic": traffic_from_profile(args.config, "paged_attention_fp8" if fp8 else "paged_attention")},
+                     "traffic": traffic_from_profile(args.config, "paged_attention_append" if use_fused else
+                                                     "paged_attention_fp8" if fp8 else "paged_attention")},
         "call_us": {"median": round(pct(attn_ms, 50) * 1e3, 3), "p10": round(pct(attn_ms, 10) * 1e3, 3),
                     "p90": round(pct(attn_ms, 90) * 1e3, 3),
-                    "hot_cache_median": round(pct(hot_ms, 50) * 1e3, 3)},
+                    "hot_cache_median": round(pct(hot_ms, 50) * 1e3, 3),
+                    "note": "event pair around each " + ("call" if use_fused else "attention call")
+                            + " in a pass after the timed region"},
     }
     log(f"step {ms_per_step * 1e3:.1f} us, attention call {attn_avg_ms * 1e3:.1f} us, "
         f"{value:.0f} GB/s step, {achieved:.0f} GB/s attention")
 
+    if use_fused and not args.no_extras:
+        # the same batch through the two separate calls, for comparison
+        nsep = args.steps
+        run_steps(3, False)
+        torch.cuda.synchronize()
+        ts0 = time.perf_counter()
+        run_steps(nsep, False)
+        torch.cuda.synchronize()
+        sep_step = (time.perf_counter() - ts0) / nsep
+        sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(30)]
+        run_steps(30, False, sev)
+        torch.cuda.synchronize()
+        sep_ms = [a.elapsed_time(b) for a, b in sev]
+        result["separate_calls"] = {"step_us": round(sep_step * 1e6, 3),
+                                    "step_GBps": round(kv_bytes / sep_step / 1e9, 2),
+                                    "attention_call_us_median": round(pct(sep_ms, 50) * 1e3, 3),
+                                    "attention_call_GBps": round(uniq_bytes / (pct(sep_ms, 50) * 1e-3) / 1e9, 2)}
     if not args.no_extras:
         result["graph"] = graph_report(pkv, copies[0], wl, torch)
         log("8-bit pools ...")
-        result["fp8"] = fp8_report(pkv, base, torch, stream, result["call_us"]["median"])
+        result["fp8"] = fp8_report(pkv, base, torch, stream, result["roofline"]["avg_call_us"])
         if len(pre):
             # the mixed batch itself: decode-only and prefill-only sub-batches
-            dms = sub_attention_ms(pkv, base, base.subset(dec), wl.scale, stream, torch)
-            dmed = pct(dms, 50)
+            dms, dmed = sub_attention_ms(pkv, base, base.subset(dec), wl.scale, stream, torch)
             ub = wl.unique_kv_read_bytes(dec)
-            result["mixed"] = {"decode_only_call_us_median": round(dmed * 1e3, 3),
+            result["mixed"] = {"decode_only_call_us_avg": round(dmed * 1e3, 3),
                                "decode_only_unique_GBps": round(ub / (dmed * 1e-3) / 1e9, 1),
                                "decode_only_logical_GBps": round(wl.kv_read_bytes(dec) / (dmed * 1e-3) / 1e9, 1),
-                               "mixed_call_us_median": result["call_us"]["median"]}
+                               "mixed_call_us_avg": result["roofline"]["avg_call_us"]}
             result["prefill"] = prefill_report(pkv, base, stream, torch)
             result["prefill"]["fp8"] = prefill_fp8_report(pkv, base, torch, stream)
-            result["mixed"]["prefill_only_call_us_median"] = result["prefill"]["call_us_median"]
+            result["mixed"]["prefill_only_call_us_avg"] = result["prefill"]["call_us_avg"]
             del copies
         else:
             del copies, base

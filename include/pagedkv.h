@@ -184,6 +184,40 @@ PKV_API int paged_attention(void* out, const void* q, const void* k_cache, const
                     void* stream);
 
 /*
+ * paged_attention_append -- kv_append and paged_attention of one step in one
+ * call, for the step's new tokens ([TGI] "Under the Hood: PagedAttention":
+ * each new token's K/V is stored in its sequence's block before attention
+ * reads the sequence; "Advanced Pattern: Kernel Fusion": the per-step cache
+ * bookkeeping is worth folding into the kernels that run anyway).
+ *
+ * The result is exactly that of
+ *     kv_append(k_new, v_new, slot_mapping, num_q_tokens, k_cache, v_cache, ...)
+ *     paged_attention(out, q, k_cache, v_cache, ...)
+ * (pools and out bit for bit) when row i of k_new / v_new is the new token of
+ * query row i -- the token at position L - q_s + j of its sequence for global
+ * row query_start_loc[s] + j -- and slot_mapping[i] is that position's slot
+ * under block_tables.  Decode rows read their new tokens from k_new / v_new
+ * directly; every row is stored into the pools within the same call, after
+ * the decode rows have read the pools and before the chunked-prefill rows do.
+ *
+ *   k_new, v_new   device, bf16 [num_q_tokens, num_kv_heads, head_dim].
+ *   slot_mapping   device, int64 [num_q_tokens]; slots < 0 or outside the
+ *                  pool are not stored (and must then not be read by
+ *                  the attention: the contract above requires real slots).
+ *   k_cache, v_cache  device, bf16 pools, written in place.
+ *   Every other argument, the workspace (same size as paged_attention's) and
+ *   the return codes are those of paged_attention.
+ */
+PKV_API int paged_attention_append(void* out, const void* q, const void* k_new, const void* v_new,
+                                   const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                                   const int32_t* block_tables, const int32_t* seq_lens,
+                                   const int32_t* query_start_loc, int32_t num_seqs, int64_t num_q_tokens,
+                                   int32_t max_blocks_per_seq, int32_t max_query_len, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                                   int32_t block_size, float scale, void* workspace, size_t* workspace_bytes,
+                                   void* stream);
+
+/*
  * 8-bit (FP8 E4M3) cache.
  *
  * [SPEED] "The KV cache: the memory problem that runs the show": quantising the

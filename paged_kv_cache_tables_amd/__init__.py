@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     AllocatorFull,
     BlockAllocator,
     PagedKVError,
+    PreparedCall,
     kv_copy_blocks,
     kv_append,
     kv_append_fp8,
@@ -20,6 +21,7 @@ from ._lib import (  # noqa: F401
     library_path,
     load_library,
     paged_attention,
+    paged_attention_append,
     paged_attention_fp8,
     workspace_bytes,
 )

@@ -50,6 +50,11 @@ def load_library() -> ctypes.CDLL:
     lib.paged_attention.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                     c_void_p, c_int32, c_int64, c_int32, c_int32, c_int32, c_int32,
                                     c_int32, c_int64, c_int32, c_float, c_void_p, c_size_p, c_void_p]
+    lib.paged_attention_append.restype = c_int
+    lib.paged_attention_append.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                           c_void_p, c_void_p, c_void_p, c_int32, c_int64, c_int32, c_int32,
+                                           c_int32, c_int32, c_int32, c_int64, c_int32, c_float, c_void_p,
+                                           c_size_p, c_void_p]
     lib.kv_append_fp8.restype = c_int
     lib.kv_append_fp8.argtypes = [c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_int64,
                                   c_int32, c_int32, c_int32, c_float, c_float, c_void_p]
@@ -118,7 +123,39 @@ def _check(t, name, dtype, ndim=None, device=None):
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
 
 
-def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None:
+_CARG = type(ctypes.byref(ctypes.c_int()))
+
+
+class PreparedCall:
+    """One library call whose tensors were checked and marshalled once: calling it issues the
+    same C call again (same tensors, same stream; their contents may have changed).  For
+    tight loops, where re-checking a dozen tensors per step costs more host time than the
+    kernels take on the device.  Holds references to its tensors."""
+
+    def __init__(self, name, fn, args, keep):
+        self.name = name
+        self._fn = fn
+        self._args = [a if a is None or isinstance(a, (ctypes._SimpleCData, _CARG)) else t(a)
+                      for t, a in zip(fn.argtypes, args)]
+        self._keep = keep
+
+    def __call__(self) -> None:
+        st = self._fn(*self._args)
+        if st != 0:
+            raise PagedKVError(self.name, st)
+
+
+def _issue(name, fn, args, prepare, keep=()):
+    """Make the C call now, or (prepare=True) return it as a PreparedCall."""
+    if prepare:
+        return PreparedCall(name, fn, args, keep)
+    st = fn(*args)
+    if st != 0:
+        raise PagedKVError(name, st)
+    return None
+
+
+def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None, prepare=False):
     """Scatter new K/V rows [T, Hkv, D] (bf16) into pools [NB, bs, Hkv, D] at slot_mapping (int64 [T])."""
     import torch
     dev = k_cache.device
@@ -133,11 +170,11 @@ def kv_append(k_new, v_new, slot_mapping, k_cache, v_cache, stream=None) -> None
     T = k_new.shape[0]
     if k_new.shape != (T, Hkv, D) or v_new.shape != (T, Hkv, D) or slot_mapping.shape[0] != T:
         raise ValueError("k_new/v_new/slot_mapping shapes do not match the pool")
-    st = load_library().kv_append(k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(), T,
-                                  k_cache.data_ptr(), v_cache.data_ptr(), NB, bs, Hkv, D,
-                                  _stream_ptr(stream, dev))
-    if st != 0:
-        raise PagedKVError("kv_append", st)
+    lib = load_library()
+    return _issue("kv_append", lib.kv_append,
+                  [k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(), T, k_cache.data_ptr(),
+                   v_cache.data_ptr(), NB, bs, Hkv, D, _stream_ptr(stream, dev)],
+                  prepare, (k_new, v_new, slot_mapping, k_cache, v_cache))
 
 
 def workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
@@ -153,21 +190,18 @@ def workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim
     return int(n.value)
 
 
-def paged_attention(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scale: float,
-                    max_query_len: int, workspace=None, stream=None) -> None:
-    """Causal GQA attention of mixed decode/prefill rows over the paged cache, written into ``out``.
-
-    out, q: bf16 [T, Hq, D]; pools bf16 [NB, bs, Hkv, D]; block_tables int32 [S, max_blocks];
-    seq_lens int32 [S]; query_start_loc int32 [S+1]; max_query_len: host bound on rows per
-    sequence.  ``workspace``: a device uint8 tensor of at least ``workspace_bytes(...)``
-    bytes (allocated here if None).
-    """
+def _attention_shapes(name, out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, pool_dtype):
+    """Check the tensors every attention call takes; return (NB, bs, Hkv, D, T, Hq, S, max_blocks, dev)."""
     import torch
     dev = k_cache.device
     _check(out, "out", torch.bfloat16, 3, dev)
     _check(q, "q", torch.bfloat16, 3, dev)
-    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
-        _check(t, n, torch.bfloat16, 4, dev)
+    if pool_dtype is None:                       # 8-bit pools
+        k_cache = _check_codes(k_cache, "k_cache", 4, dev)
+        v_cache = _check_codes(v_cache, "v_cache", 4, dev)
+    else:
+        for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+            _check(t, n, pool_dtype, 4, dev)
     _check(block_tables, "block_tables", torch.int32, 2, dev)
     _check(seq_lens, "seq_lens", torch.int32, 1, dev)
     _check(query_start_loc, "query_start_loc", torch.int32, 1, dev)
@@ -178,24 +212,76 @@ def paged_attention(out, q, k_cache, v_cache, block_tables, seq_lens, query_star
         raise ValueError("q/out/pool shapes do not match")
     if query_start_loc.shape[0] != S + 1 or block_tables.shape[0] != S:
         raise ValueError("query_start_loc must be [S+1] and block_tables [S, max_blocks]")
-    max_blocks = block_tables.shape[1]
+    return NB, bs, Hkv, D, T, Hq, S, block_tables.shape[1], dev
+
+
+def _workspace(name, need, workspace, dev):
+    import torch
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    else:
+        _check(workspace, "workspace", torch.uint8, 1, dev)
+    return workspace
+
+
+def paged_attention(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scale: float,
+                    max_query_len: int, workspace=None, stream=None, prepare=False):
+    """Causal GQA attention of mixed decode/prefill rows over the paged cache, written into ``out``.
+
+    out, q: bf16 [T, Hq, D]; pools bf16 [NB, bs, Hkv, D]; block_tables int32 [S, max_blocks];
+    seq_lens int32 [S]; query_start_loc int32 [S+1]; max_query_len: host bound on rows per
+    sequence.  ``workspace``: a device uint8 tensor of at least ``workspace_bytes(...)``
+    bytes (allocated here if None; it needs no initialisation).  ``prepare=True`` returns
+    the checked call as a PreparedCall instead of making it.
+    """
+    import torch
+    NB, bs, Hkv, D, T, Hq, S, max_blocks, dev = _attention_shapes(
+        "paged_attention", out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, torch.bfloat16)
     lib = load_library()
     need = ctypes.c_size_t(0)
     st = lib.paged_attention(None, None, None, None, None, None, None, S, T, max_blocks, max_query_len,
                              Hq, Hkv, D, NB, bs, float(scale), None, ctypes.byref(need), None)
     if st != 0:
         raise PagedKVError("paged_attention", st)
-    if workspace is None:
-        workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)
-    else:
-        _check(workspace, "workspace", torch.uint8, 1, dev)
+    workspace = _workspace("paged_attention", need.value, workspace, dev)
     have = ctypes.c_size_t(workspace.numel())
-    st = lib.paged_attention(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                             block_tables.data_ptr(), seq_lens.data_ptr(), query_start_loc.data_ptr(),
-                             S, T, max_blocks, max_query_len, Hq, Hkv, D, NB, bs, float(scale),
-                             workspace.data_ptr(), ctypes.byref(have), _stream_ptr(stream, dev))
+    return _issue("paged_attention", lib.paged_attention,
+                  [out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+                   seq_lens.data_ptr(), query_start_loc.data_ptr(), S, T, max_blocks, max_query_len, Hq, Hkv, D,
+                   NB, bs, float(scale), workspace.data_ptr(), ctypes.byref(have), _stream_ptr(stream, dev)],
+                  prepare, (out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, workspace, have))
+
+
+def paged_attention_append(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, seq_lens,
+                           query_start_loc, scale: float, max_query_len: int, workspace=None, stream=None,
+                           prepare=False):
+    """kv_append then paged_attention in one call: row i of k_new / v_new (bf16 [T, Hkv, D]) is the new
+    token of query row i and slot_mapping[i] (int64 [T]) its slot under block_tables.  Same result as
+    the two calls; the workspace is sized as for paged_attention (``workspace_bytes``)."""
+    import torch
+    NB, bs, Hkv, D, T, Hq, S, max_blocks, dev = _attention_shapes(
+        "paged_attention_append", out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
+        torch.bfloat16)
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _check(t, n, torch.bfloat16, 3, dev)
+    _check(slot_mapping, "slot_mapping", torch.int64, 1, dev)
+    if k_new.shape != (T, Hkv, D) or v_new.shape != (T, Hkv, D) or slot_mapping.shape[0] != T:
+        raise ValueError("k_new/v_new/slot_mapping must have one row per query row")
+    lib = load_library()
+    need = ctypes.c_size_t(0)
+    st = lib.paged_attention(None, None, None, None, None, None, None, S, T, max_blocks, max_query_len,
+                             Hq, Hkv, D, NB, bs, float(scale), None, ctypes.byref(need), None)
     if st != 0:
-        raise PagedKVError("paged_attention", st)
+        raise PagedKVError("paged_attention_append", st)
+    workspace = _workspace("paged_attention_append", need.value, workspace, dev)
+    have = ctypes.c_size_t(workspace.numel())
+    return _issue("paged_attention_append", lib.paged_attention_append,
+                  [out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(),
+                   k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), seq_lens.data_ptr(),
+                   query_start_loc.data_ptr(), S, T, max_blocks, max_query_len, Hq, Hkv, D, NB, bs, float(scale),
+                   workspace.data_ptr(), ctypes.byref(have), _stream_ptr(stream, dev)],
+                  prepare, (out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, seq_lens,
+                            query_start_loc, workspace, have))
 
 
 def _check_codes(t, name, ndim, device):
@@ -208,7 +294,7 @@ def _check_codes(t, name, ndim, device):
 
 
 def kv_append_fp8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale: float, v_scale: float,
-                  stream=None) -> None:
+                  stream=None, prepare=False):
     """Quantise new K/V rows [T, Hkv, D] (bf16) into E4M3 pools [NB, bs, Hkv, D] (uint8) at slot_mapping."""
     import torch
     dev = k_cache.device
@@ -223,35 +309,23 @@ def kv_append_fp8(k_new, v_new, slot_mapping, k_cache, v_cache, k_scale: float, 
     T = k_new.shape[0]
     if k_new.shape != (T, Hkv, D) or v_new.shape != (T, Hkv, D) or slot_mapping.shape[0] != T:
         raise ValueError("k_new/v_new/slot_mapping shapes do not match the pool")
-    st = load_library().kv_append_fp8(k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(), T,
-                                      k_cache.data_ptr(), v_cache.data_ptr(), NB, bs, Hkv, D,
-                                      float(k_scale), float(v_scale), _stream_ptr(stream, dev))
-    if st != 0:
-        raise PagedKVError("kv_append_fp8", st)
+    lib = load_library()
+    return _issue("kv_append_fp8", lib.kv_append_fp8,
+                  [k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(), T, k_cache.data_ptr(),
+                   v_cache.data_ptr(), NB, bs, Hkv, D, float(k_scale), float(v_scale), _stream_ptr(stream, dev)],
+                  prepare, (k_new, v_new, slot_mapping, k_cache, v_cache))
 
 
 def paged_attention_fp8(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scale: float,
                         max_query_len: int, k_scale: float, v_scale: float, workspace=None,
-                        stream=None) -> None:
+                        stream=None, prepare=False):
     """paged_attention over E4M3 pools (uint8 [NB, bs, Hkv, D]) with per-pool scales k_scale, v_scale.
     The workspace is sized as for paged_attention (``workspace_bytes``)."""
+    NB, bs, Hkv, D, T, Hq, S, max_blocks, dev = _attention_shapes(
+        "paged_attention_fp8", out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, None)
     import torch
-    dev = k_cache.device
-    _check(out, "out", torch.bfloat16, 3, dev)
-    _check(q, "q", torch.bfloat16, 3, dev)
-    k_cache = _check_codes(k_cache, "k_cache", 4, dev)
-    v_cache = _check_codes(v_cache, "v_cache", 4, dev)
-    _check(block_tables, "block_tables", torch.int32, 2, dev)
-    _check(seq_lens, "seq_lens", torch.int32, 1, dev)
-    _check(query_start_loc, "query_start_loc", torch.int32, 1, dev)
-    NB, bs, Hkv, D = k_cache.shape
-    T, Hq, Dq = q.shape
-    S = seq_lens.shape[0]
-    if Dq != D or out.shape != q.shape or v_cache.shape != k_cache.shape:
-        raise ValueError("q/out/pool shapes do not match")
-    if query_start_loc.shape[0] != S + 1 or block_tables.shape[0] != S:
-        raise ValueError("query_start_loc must be [S+1] and block_tables [S, max_blocks]")
-    max_blocks = block_tables.shape[1]
+    if k_cache.dtype == torch.float8_e4m3fn:
+        k_cache, v_cache = k_cache.view(torch.uint8), v_cache.view(torch.uint8)
     lib = load_library()
     need = ctypes.c_size_t(0)
     st = lib.paged_attention_fp8(None, None, None, None, None, None, None, S, T, max_blocks, max_query_len,
@@ -259,18 +333,14 @@ def paged_attention_fp8(out, q, k_cache, v_cache, block_tables, seq_lens, query_
                                  ctypes.byref(need), None)
     if st != 0:
         raise PagedKVError("paged_attention_fp8", st)
-    if workspace is None:
-        workspace = torch.empty(need.value, dtype=torch.uint8, device=dev)
-    else:
-        _check(workspace, "workspace", torch.uint8, 1, dev)
+    workspace = _workspace("paged_attention_fp8", need.value, workspace, dev)
     have = ctypes.c_size_t(workspace.numel())
-    st = lib.paged_attention_fp8(out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                                 block_tables.data_ptr(), seq_lens.data_ptr(), query_start_loc.data_ptr(),
-                                 S, T, max_blocks, max_query_len, Hq, Hkv, D, NB, bs, float(scale),
-                                 float(k_scale), float(v_scale), workspace.data_ptr(), ctypes.byref(have),
-                                 _stream_ptr(stream, dev))
-    if st != 0:
-        raise PagedKVError("paged_attention_fp8", st)
+    return _issue("paged_attention_fp8", lib.paged_attention_fp8,
+                  [out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
+                   seq_lens.data_ptr(), query_start_loc.data_ptr(), S, T, max_blocks, max_query_len, Hq, Hkv, D,
+                   NB, bs, float(scale), float(k_scale), float(v_scale), workspace.data_ptr(), ctypes.byref(have),
+                   _stream_ptr(stream, dev)],
+                  prepare, (out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, workspace, have))
 
 
 def kv_copy_blocks(k_cache, v_cache, src, dst, stream=None) -> None:

@@ -165,7 +165,8 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
                    int32_t num_seqs, int64_t num_q_tokens, int32_t max_blocks_per_seq, int32_t max_query_len,
                    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
                    int32_t block_size, float scale, bool fp8, float k_scale, float v_scale, void* workspace,
-                   size_t* workspace_bytes, void* stream) {
+                   size_t* workspace_bytes, void* stream, const void* k_new = nullptr,
+                   const void* v_new = nullptr, const int64_t* slot_mapping = nullptr, bool fused = false) {
   if (!workspace_bytes) return PKV_EINVAL;
   if (fp8 && !(isfinite(k_scale) && k_scale > 0.f && isfinite(v_scale) && v_scale > 0.f)) return PKV_EINVAL;
   if (num_seqs < 0 || num_q_tokens < 0 || max_blocks_per_seq < 1 || max_query_len < 0 ||
@@ -195,6 +196,10 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
   if (max_query_len < 1) return PKV_EINVAL;   // rows exist, so some sequence has q_s >= 1
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
     return PKV_EINVAL;
+  if (fused && (!k_new || !v_new || !slot_mapping || !aligned(k_new, 16) || !aligned(v_new, 16) ||
+                !aligned(slot_mapping, 8)))
+    return PKV_EINVAL;
+  if (fused && num_blocks > INT64_MAX / block_size) return PKV_EINVAL;
 
   pkv::AttnParams p{};
   p.out = (uint16_t*)out;
@@ -216,6 +221,13 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
   p.scale_log2 = scale * 1.4426950408889634f;
   if (fp8) p.scale_log2 *= k_scale;               // scores of codes, times the K scale
   p.v_scale = fp8 ? v_scale : 1.f;
+  if (fused) {
+    p.k_new = (const uint16_t*)k_new;
+    p.v_new = (const uint16_t*)v_new;
+    p.slots = slot_mapping;
+    p.k_pool = (uint4*)k_cache;
+    p.v_pool = (uint4*)v_cache;
+  }
   p.decode_waves = decode_waves_for_current_device();
   // the KV heads a decode workgroup reads together: the largest power of two <= 8 dividing Hkv
   p.decode_group = 1;
@@ -259,6 +271,19 @@ int paged_attention(void* out, const void* q, const void* k_cache, const void* v
   return attention_impl(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, num_seqs,
                         num_q_tokens, max_blocks_per_seq, max_query_len, num_q_heads, num_kv_heads, head_dim,
                         num_blocks, block_size, scale, false, 1.f, 1.f, workspace, workspace_bytes, stream);
+}
+
+int paged_attention_append(void* out, const void* q, const void* k_new, const void* v_new,
+                           const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                           const int32_t* block_tables, const int32_t* seq_lens,
+                           const int32_t* query_start_loc, int32_t num_seqs, int64_t num_q_tokens,
+                           int32_t max_blocks_per_seq, int32_t max_query_len, int32_t num_q_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, int32_t block_size,
+                           float scale, void* workspace, size_t* workspace_bytes, void* stream) {
+  return attention_impl(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, num_seqs,
+                        num_q_tokens, max_blocks_per_seq, max_query_len, num_q_heads, num_kv_heads, head_dim,
+                        num_blocks, block_size, scale, false, 1.f, 1.f, workspace, workspace_bytes, stream,
+                        k_new, v_new, slot_mapping, true);
 }
 
 int paged_attention_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,

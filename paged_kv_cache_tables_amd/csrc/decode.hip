@@ -44,6 +44,9 @@
 //     its contents are in LDS, so K and V both run one tile ahead.
 //   A piece that covers its whole (sequence, head) writes bf16 output directly;
 //   otherwise fp32 partials (O, m, l) go to the workspace for the merge kernel.
+#include <algorithm>
+#include <climits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -183,6 +186,11 @@ void decode_kernel(AttnParams p) {
     const int* bt_row = p.block_tables + (size_t)s * p.max_blocks;
     const char* kbase = p.k_cache + (size_t)h * D * EB;
     const char* vbase = p.v_cache + (size_t)h * D * EB;
+    // positions fresh0 .. L - 1 are this step's tokens; with a fused append they are not in
+    // the pools yet and come from the rows of k_new / v_new instead
+    const int fresh0 = (!F8 && p.k_new != nullptr) ? L - cur_q : INT_MAX;
+    const uint16_t* knew_h = p.k_new + (size_t)h * D;
+    const uint16_t* vnew_h = p.v_new + (size_t)h * D;
 
     // ---- Q^T as the B operand: column n, dims ks*32 + kg*8 .. +8 (zero for padding columns) ----
     bf16x8 qreg[KS];
@@ -210,8 +218,21 @@ void decode_kernel(AttnParams p) {
         dst[j] = (unsigned)b < (unsigned)nblocks ? b : 0;
       }
     };
-    // Coalesced tile load: load i covers rows RPI*i .. RPI*i + RPI - 1 (one pool block).
-    auto issue = [&](const char* base, const int* bb, uint4* reg) {
+    // Coalesced tile load: load i covers rows RPI*i .. RPI*i + RPI - 1 (one pool block).  A
+    // tile that holds fresh positions takes those rows from the new rows instead (lane by lane).
+    auto issue = [&](const char* base, const uint16_t* nbase, const int* bb, uint4* reg, int t0) {
+      if (t0 + kTile > fresh0) {
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+          const char* b = base + (size_t)bb[(RPI * i) / BS] * blk_bytes + (uint32_t)((RPI * i) % BS) * row_bytes;
+          const int t = t0 + RPI * i + lrow;
+          const char* src = b + lane_off;
+          if (t >= fresh0 && t < L)
+            src = reinterpret_cast<const char*>(nbase + (size_t)(row0 + t - fresh0) * row_stride) + lch * 16;
+          reg[i] = load_stream16(src);
+        }
+        return;
+      }
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const char* b = base + (size_t)bb[(RPI * i) / BS] * blk_bytes + (uint32_t)((RPI * i) % BS) * row_bytes;
@@ -241,8 +262,8 @@ void decode_kernel(AttnParams p) {
     int bts[NBT];
     load_bts(t_begin, bts);
     uint4 kreg[NL], vreg[NL];
-    issue(kbase, bts, kreg);
-    issue(vbase, bts, vreg);
+    issue(kbase, knew_h, bts, kreg, t_begin);
+    issue(vbase, vnew_h, bts, vreg, t_begin);
     for (int tile_i = 0; tile_i < ntiles; ++tile_i) {
       const int ts = t_begin + tile_i * kTile;
       const int nvalid = min(kTile, t_end - ts);
@@ -255,7 +276,7 @@ void decode_kernel(AttnParams p) {
       // ---- K tile -> LDS; refill the K registers with the next tile ----
       stage(kreg, nvalid);
       __builtin_amdgcn_sched_barrier(0);
-      if (has_next) issue(kbase, bts_next, kreg);
+      if (has_next) issue(kbase, knew_h, bts_next, kreg, ts + kTile);
       wave_lds_sync();
 
       // ---- S^T = K Q^T ----
@@ -275,7 +296,7 @@ void decode_kernel(AttnParams p) {
       // ---- V tile -> LDS; refill the V registers with the next tile ----
       stage(vreg, nvalid);
       __builtin_amdgcn_sched_barrier(0);
-      if (has_next) issue(vbase, bts_next, vreg);
+      if (has_next) issue(vbase, vnew_h, bts_next, vreg, ts + kTile);
 
       // ---- online softmax for column n over this tile's tokens (exp2 domain) ----
       const int last = MULTI ? min(nvalid - 1, lim - ts) : nvalid - 1;   // last token column n sees
@@ -400,7 +421,8 @@ void decode_kernel(AttnParams p) {
 // out = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j with M = max_j m_j.
 // A piece row of D floats is D / 4 lanes of float4, so a wave reads 64 / (D / 4) pieces
 // at once and adds its lane groups with lane exchanges.  Narrow form: one wave per
-// (sequence, query head), four per workgroup, for calls whose segments have few pieces.
+// (sequence, query head), four per workgroup, for calls whose segments have few pieces;
+// one pass with a running max, several steps of loads in flight.
 // Wide form: the four waves of a workgroup share one (sequence, query head) and are
 // combined through LDS, for long sequences cut into many pieces.
 constexpr int kMergeWaves = 4;
@@ -412,17 +434,115 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(AttnParams p
   constexpr int WPC = WIDE ? kMergeWaves : 1;    // waves per (sequence, query head)
   __shared__ float4 part[WIDE ? kMergeWaves : 1][LPP];
   __shared__ float lpart[WIDE ? kMergeWaves : 1];
+  if ((int)blockIdx.x >= p.merge_blocks) {       // fused append: scatter the new rows into the pools
+    // one thread per 16-byte chunk of a K or V row, grid-stride over the append workgroups
+    const int row_chunks = p.Hkv * D / 8;
+    const int64_t per_token = 2 * (int64_t)row_chunks;
+    const int64_t total = p.num_q_tokens * per_token;
+    const int64_t nthreads = (int64_t)(gridDim.x - p.merge_blocks) * blockDim.x;
+    const int64_t num_slots = p.num_blocks * p.bs;
+    for (int64_t idx = (int64_t)(blockIdx.x - p.merge_blocks) * blockDim.x + threadIdx.x; idx < total;
+         idx += nthreads) {
+      const int64_t i = idx / per_token;
+      const int rem = (int)(idx - i * per_token);
+      const int which = rem >= row_chunks;       // 0 = K, 1 = V
+      const int c = rem - which * row_chunks;
+      const int64_t slot = p.slots[i];
+      if (slot < 0 || slot >= num_slots) continue;   // padding row, or outside the pool
+      const uint4* src = reinterpret_cast<const uint4*>(which ? p.v_new : p.k_new);
+      uint4* dst = which ? p.v_pool : p.k_pool;
+      dst[slot * row_chunks + c] = src[i * row_chunks + c];
+    }
+    return;
+  }
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = (int)(threadIdx.x / kWave);
   // cell = (sequence s, query head qh); its decode rows are merged one after the other
   const int cell = WIDE ? (int)blockIdx.x : (int)blockIdx.x * kMergeWaves + wv;
   if (cell >= p.num_seqs * p.Hq) return;         // uniform over the workgroup in the wide form
   const int s = cell / p.Hq, qh = cell % p.Hq;
+  const int sub = lane / LPP, dq = lane % LPP;
+  if constexpr (!WIDE) {
+    // One pass with a running max, CK wave-wide steps (PPI pieces each) of loads in flight
+    // at a time.  The first round of row 0 is loaded together with the sequence's lengths
+    // and piece count (indices clamped into the row's pieces, so always in the workspace);
+    // pieces past the count are discarded by selection, never by a zero weight.
+    constexpr int CK = 4;
+    auto merge_row = [&](int rr, int nsplit, int row0, const float4* o0, const float* m0, const float* l0) {
+      const size_t base = (((size_t)s * p.decode_max_q + rr) * p.Hq + qh) * p.max_splits;
+      float M = -INFINITY, ls = 0.f;
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int j0 = 0; j0 < nsplit; j0 += CK * PPI) {
+        float4 o[CK];
+        float mj[CK], lj[CK];
+#pragma unroll
+        for (int c = 0; c < CK; ++c) {
+          if (o0 && j0 == 0) {
+            o[c] = o0[c]; mj[c] = m0[c]; lj[c] = l0[c];
+          } else {
+            const int j = min(j0 + c * PPI + sub, p.max_splits - 1);
+            mj[c] = p.ws_m[base + j];
+            lj[c] = p.ws_l[base + j];
+            o[c] = *reinterpret_cast<const float4*>(p.ws_o + (base + j) * D + 4 * dq);
+          }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int c = 0; c < CK; ++c)
+          if (j0 + c * PPI + sub < nsplit) mx = fmaxf(mx, mj[c]);
+#pragma unroll
+        for (int off = LPP; off < kWave; off *= 2) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
+        const float Mn = fmaxf(M, mx);           // finite: piece 0 holds key 0, seen by every row
+        const float r = fast_exp2(M - Mn);       // 0 on the first round
+        M = Mn;
+        ls *= r;
+        acc.x *= r; acc.y *= r; acc.z *= r; acc.w *= r;
+#pragma unroll
+        for (int c = 0; c < CK; ++c) {
+          if (j0 + c * PPI + sub < nsplit) {
+            const float f = fast_exp2(mj[c] - M);   // 0 for a piece that saw no key of this row
+            acc.x = fmaf(f, o[c].x, acc.x); acc.y = fmaf(f, o[c].y, acc.y);
+            acc.z = fmaf(f, o[c].z, acc.z); acc.w = fmaf(f, o[c].w, acc.w);
+            ls = fmaf(f, lj[c], ls);
+          }
+        }
+      }
+#pragma unroll
+      for (int off = LPP; off < kWave; off *= 2) {
+        acc.x += __shfl_xor(acc.x, off, kWave); acc.y += __shfl_xor(acc.y, off, kWave);
+        acc.z += __shfl_xor(acc.z, off, kWave); acc.w += __shfl_xor(acc.w, off, kWave);
+        ls += __shfl_xor(ls, off, kWave);
+      }
+      if (sub == 0) {
+        const float inv = 1.f / ls;
+        const uint32_t w0 = (uint32_t)f32_to_bf16_rne(acc.x * inv) | ((uint32_t)f32_to_bf16_rne(acc.y * inv) << 16);
+        const uint32_t w1 = (uint32_t)f32_to_bf16_rne(acc.z * inv) | ((uint32_t)f32_to_bf16_rne(acc.w * inv) << 16);
+        *reinterpret_cast<uint2*>(p.out + ((size_t)(row0 + rr) * p.Hq + qh) * D + 4 * dq) = make_uint2(w0, w1);
+      }
+    };
+    float4 o0[CK];
+    float m0[CK], l0[CK];
+    {
+      const size_t base = ((size_t)s * p.decode_max_q * p.Hq + qh) * p.max_splits;   // row 0
+#pragma unroll
+      for (int c = 0; c < CK; ++c) {
+        const int j = min(c * PPI + sub, p.max_splits - 1);
+        m0[c] = p.ws_m[base + j];
+        l0[c] = p.ws_l[base + j];
+        o0[c] = *reinterpret_cast<const float4*>(p.ws_o + (base + j) * D + 4 * dq);
+      }
+    }
+    const int nsplit = p.ws_nparts[(size_t)s * p.Hkv + qh / (p.Hq / p.Hkv)];
+    const SeqInfo si = seq_info(p, s);
+    if (si.tiles == 0 || nsplit <= 1) return;    // no decode rows, or written by the decode kernel
+    merge_row(0, nsplit, si.row0, o0, m0, l0);
+    for (int rr = 1; rr < si.q; ++rr) merge_row(rr, nsplit, si.row0, nullptr, nullptr, nullptr);
+    return;
+  }
   const SeqInfo si = seq_info(p, s);
   if (si.tiles == 0) return;                     // no decode rows (or nothing to attend)
   const int nsplit = p.ws_nparts[(size_t)s * p.Hkv + qh / (p.Hq / p.Hkv)];
   if (nsplit <= 1) return;                       // written directly by the decode kernel
-  const int sub = lane / LPP, dq = lane % LPP;
   const int w_in = WIDE ? wv : 0;
 
   for (int rr = 0; rr < si.q; ++rr) {
@@ -529,14 +649,22 @@ hipError_t launch_merge(const AttnParams& p, hipStream_t stream) {
   // among the waves of a workgroup there
   const int64_t cells = (int64_t)p.num_seqs * p.Hq;
   const bool wide = p.max_splits > 32;
-  const dim3 grid((unsigned)(wide ? cells : (cells + kMergeWaves - 1) / kMergeWaves));
+  AttnParams q = p;
+  q.merge_blocks = (int)(wide ? cells : (cells + kMergeWaves - 1) / kMergeWaves);
+  // fused append: one more workgroup per 256 chunks of new rows (at most 4096; they stride)
+  int64_t append_blocks = 0;
+  if (p.k_new) {
+    const int64_t chunks = p.num_q_tokens * 2 * ((int64_t)p.Hkv * p.D / 8);
+    append_blocks = std::min<int64_t>((chunks + kMergeWaves * kWave - 1) / (kMergeWaves * kWave), 4096);
+  }
+  const dim3 grid((unsigned)(q.merge_blocks + append_blocks));
   const dim3 block(kMergeWaves * kWave);
   if (p.D == 128) {
-    if (wide) hipLaunchKernelGGL((merge_kernel<128, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((merge_kernel<128, false>), grid, block, 0, stream, p);
+    if (wide) hipLaunchKernelGGL((merge_kernel<128, true>), grid, block, 0, stream, q);
+    else hipLaunchKernelGGL((merge_kernel<128, false>), grid, block, 0, stream, q);
   } else if (p.D == 64) {
-    if (wide) hipLaunchKernelGGL((merge_kernel<64, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((merge_kernel<64, false>), grid, block, 0, stream, p);
+    if (wide) hipLaunchKernelGGL((merge_kernel<64, true>), grid, block, 0, stream, q);
+    else hipLaunchKernelGGL((merge_kernel<64, false>), grid, block, 0, stream, q);
   } else {
     return hipErrorInvalidValue;
   }

@@ -33,6 +33,15 @@ struct AttnParams {
   float* ws_m;                    // [num_seqs, decode_max_q, Hq, max_splits]     partial max (exp2 domain)
   float* ws_l;                    // [num_seqs, decode_max_q, Hq, max_splits]     partial sum of exponentials
   int* ws_nparts;                 // [num_seqs, Hkv]                pieces of each decode (sequence, head)
+  // fused append (paged_attention_append; null k_new otherwise): row i of k_new / v_new is the
+  // new token of query row i, stored at slot slots[i].  Decode rows read this step's tokens
+  // from k_new / v_new; the merge launch scatters every row into the pools afterwards.
+  const uint16_t* k_new;          // bf16 [num_q_tokens, Hkv, D]
+  const uint16_t* v_new;
+  const int64_t* slots;           // [num_q_tokens]; < 0 or >= num_blocks * bs: not stored
+  uint4* k_pool;                  // the pools, writable
+  uint4* v_pool;
+  int merge_blocks;               // merge launch: workgroups that merge (the rest append)
   int2* plan_items;               // prefill work list (sequence, row tile), written by the planner
   int* plan_count;                // number of valid items
   int plan_capacity;              // items the workspace holds

@@ -206,3 +206,44 @@ def test_paged_attention_fp8_checks_pointers_before_launch(lib):
     for field in ("out", "q", "k_cache", "v_cache", "block_tables", "seq_lens", "qsl"):
         args = attn_fp8_args(workspace=FAKE, workspace_bytes=ctypes.byref(n), **{field: None})
         assert lib.paged_attention_fp8(*args) == PKV_EINVAL, field
+
+
+def attn_append_args(**over):
+    n = ctypes.c_size_t(1 << 30)
+    a = dict(out=FAKE, q=FAKE, k_new=FAKE, v_new=FAKE, slot_mapping=FAKE, k_cache=FAKE, v_cache=FAKE,
+             block_tables=FAKE, seq_lens=FAKE, qsl=FAKE, num_seqs=4, num_q_tokens=8, max_blocks=4,
+             max_query_len=5, Hq=4, Hkv=2, D=64, num_blocks=64, bs=16, scale=0.125, workspace=None,
+             workspace_bytes=ctypes.byref(n), stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+def test_paged_attention_append_workspace_matches(lib):
+    a, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.paged_attention(*attn_args(workspace_bytes=ctypes.byref(a))) == PKV_OK
+    assert lib.paged_attention_append(*attn_append_args(workspace_bytes=ctypes.byref(b))) == PKV_OK
+    assert a.value == b.value
+
+
+@pytest.mark.parametrize("over,expect", [
+    (dict(workspace_bytes=None), PKV_EINVAL),
+    (dict(Hq=6, Hkv=4), PKV_EINVAL),
+    (dict(D=96), PKV_EUNSUPPORTED),
+    (dict(bs=12), PKV_EUNSUPPORTED),
+    (dict(scale=float("nan")), PKV_EINVAL),
+])
+def test_paged_attention_append_validation(lib, over, expect):
+    assert lib.paged_attention_append(*attn_append_args(**over)) == expect
+
+
+def test_paged_attention_append_checks_pointers_before_launch(lib):
+    n = ctypes.c_size_t(1 << 30)
+    for field in ("out", "q", "k_new", "v_new", "slot_mapping", "k_cache", "v_cache", "block_tables",
+                  "seq_lens", "qsl"):
+        args = attn_append_args(workspace=FAKE, workspace_bytes=ctypes.byref(n), **{field: None})
+        assert lib.paged_attention_append(*args) == PKV_EINVAL, field
+    for field, off in (("k_new", 8), ("v_new", 8), ("slot_mapping", 4)):
+        args = attn_append_args(workspace=FAKE, workspace_bytes=ctypes.byref(n), **{field: FAKE + off})
+        assert lib.paged_attention_append(*args) == PKV_EINVAL, field   # misaligned
+    args = attn_append_args(workspace=FAKE, workspace_bytes=ctypes.byref(n), num_q_tokens=0)
+    assert lib.paged_attention_append(*args) == PKV_OK                 # empty batch: no launch

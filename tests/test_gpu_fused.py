@@ -1,0 +1,127 @@
+"""GPU parity of paged_attention_append, the fused kv_append + paged_attention call.
+
+Its contract is the two calls' result, bit for bit: on the same seeded inputs
+the fused call must leave the pools and the output exactly as kv_append
+followed by paged_attention does (over the whole pool), and the output is
+also checked against the float64 oracle under the usual tolerance.  Row i of
+k_new / v_new is the new token of query row i (the workloads' ordering).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_harness import DeviceBatch, compare, to_host_bits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    import paged_kv_cache_tables_amd as pkv
+    pkv.load_library()
+    return torch
+
+
+def fused(db, workspace=None):
+    import paged_kv_cache_tables_amd as pkv
+    pkv.paged_attention_append(db.out, db.q, db.k_new, db.v_new, db.slots, db.k_cache, db.v_cache, db.bt,
+                               db.seq_lens, db.qsl, db.wl.scale, db.wl.max_query_len, workspace=workspace)
+
+
+def check_fused_equals_separate(wl, label, oracle_rows="all"):
+    import torch
+    print(f"fused vs separate: {label}", flush=True)
+    sep, fus = DeviceBatch(wl), DeviceBatch(wl)
+    sep.step()                                    # kv_append, then paged_attention
+    fused(fus)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_bits(fus.k_cache), to_host_bits(sep.k_cache)), "K pool differs"
+    assert np.array_equal(to_host_bits(fus.v_cache), to_host_bits(sep.v_cache)), "V pool differs"
+    out = to_host_bits(fus.out)
+    assert np.array_equal(out, to_host_bits(sep.out)), "output differs from the two separate calls"
+    if oracle_rows is not None:
+        rows = None if oracle_rows == "all" else oracle_rows
+        k2, v2 = oracle.kv_append(wl.k_cache, wl.v_cache, wl.k_new, wl.v_new, wl.slot_mapping)
+        ref = oracle.paged_attention(wl.q, k2, v2, wl.block_tables, wl.seq_lens, wl.query_start_loc,
+                                     wl.num_kv_heads, wl.scale, rows=rows)
+        compare(out, ref, rows=rows, label=f"fused-{label}")
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+def test_fused_equals_separate_calls(cfg):
+    wl = W.make_config(cfg)
+    rows = "all"
+    if cfg in (2, 3):                             # big batches: the oracle checks a sample
+        rng = np.random.default_rng(cfg)
+        rows = sorted(rng.choice(wl.num_q_tokens, size=min(96, wl.num_q_tokens), replace=False).tolist())
+    check_fused_equals_separate(wl, f"config{cfg}", oracle_rows=rows)
+
+
+FUSED_EDGE = [
+    ("bs8-mixed", [(1, 1), (9, 1), (700, 1), (130, 3), (300, 300)], 8, 2, 128, 8),
+    ("bs32-g8", [(33, 1), (1025, 1), (2000, 64), (64, 64)], 16, 2, 128, 32),
+    ("d64-mha", [(5, 1), (513, 1), (100, 37), (1, 1)], 4, 4, 64, 16),
+    ("multi-row-g4", [(700, 4), (5, 2), (1300, 3), (64, 4), (2, 2), (900, 1)], 16, 4, 128, 16),
+    ("block-boundary", [(16, 1), (17, 1), (64, 1), (65, 1), (32, 2), (80, 16)], 8, 8, 128, 16),
+    ("long-many-pieces", [(100000, 1), (3, 1)], 8, 2, 128, 16),
+]
+
+
+@pytest.mark.parametrize("name,specs,Hq,Hkv,D,bs", FUSED_EDGE, ids=[e[0] for e in FUSED_EDGE])
+def test_fused_edge_shapes(name, specs, Hq, Hkv, D, bs):
+    check_fused_equals_separate(W.custom(name, specs, Hq, Hkv, D, bs, seed=len(name) + 7), name)
+
+
+def test_fused_rows_out_of_order_and_empty_sequences():
+    specs = [(40, 1), (25, 0), (300, 20), (9, 0), (1, 1), (200, 1)]
+    wl = W.custom("fused-zero-rows", specs, 8, 2, 128, 16, seed=5, row_order=[3, 0, 5, 2, 1, 4])
+    check_fused_equals_separate(wl, "zero-rows")
+
+
+def test_fused_step_captured_in_hip_graph(gpu):
+    """The fused step captured once and replayed: each replay (fresh pools and queries written
+    by eager work in between) equals the eager fused call bit for bit."""
+    torch = gpu
+    import paged_kv_cache_tables_amd as pkv
+    wl = W.config1(num_seqs=16)
+    db = DeviceBatch(wl)
+    k0, v0 = db.k_cache.clone(), db.v_cache.clone()
+    need = pkv.workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                               wl.max_blocks_per_seq, wl.block_size, wl.max_query_len)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda:0")
+    q_alt = [db.q.clone(), torch.flip(db.q, dims=[1]).contiguous()]
+
+    def reset(qv):
+        db.k_cache.copy_(k0)
+        db.v_cache.copy_(v0)
+        db.q.copy_(qv)
+        db.out.zero_()
+
+    want = []
+    for qv in q_alt:
+        reset(qv)
+        fused(db, ws)
+        torch.cuda.synchronize()
+        want.append((to_host_bits(db.out), to_host_bits(db.k_cache)))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fused(db, ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fused(db, ws)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        i = rep % len(q_alt)
+        reset(q_alt[i])
+        ws.fill_(0xA5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host_bits(db.out), want[i][0]), f"replay {rep} output differs"
+        assert np.array_equal(to_host_bits(db.k_cache), want[i][1]), f"replay {rep} pool differs"
