@@ -464,11 +464,10 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(AttnParams p
   const int sub = lane / LPP, dq = lane % LPP;
   if constexpr (!WIDE) {
     // One pass with a running max, CK wave-wide steps (PPI pieces each) of loads in flight
-    // at a time.  The first round of row 0 is loaded together with the sequence's lengths
-    // and piece count (indices clamped into the row's pieces, so always in the workspace);
-    // pieces past the count are discarded by selection, never by a zero weight.
+    // at a time; lanes past the piece count load nothing and are discarded by selection,
+    // never by a zero weight.
     constexpr int CK = 4;
-    auto merge_row = [&](int rr, int nsplit, int row0, const float4* o0, const float* m0, const float* l0) {
+    auto merge_row = [&](int rr, int nsplit, int row0) {
       const size_t base = (((size_t)s * p.decode_max_q + rr) * p.Hq + qh) * p.max_splits;
       float M = -INFINITY, ls = 0.f;
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -477,10 +476,11 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(AttnParams p
         float mj[CK], lj[CK];
 #pragma unroll
         for (int c = 0; c < CK; ++c) {
-          if (o0 && j0 == 0) {
-            o[c] = o0[c]; mj[c] = m0[c]; lj[c] = l0[c];
-          } else {
-            const int j = min(j0 + c * PPI + sub, p.max_splits - 1);
+          const int j = j0 + c * PPI + sub;
+          mj[c] = -INFINITY;
+          lj[c] = 0.f;
+          o[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (j < nsplit) {                      // only the pieces that exist are read
             mj[c] = p.ws_m[base + j];
             lj[c] = p.ws_l[base + j];
             o[c] = *reinterpret_cast<const float4*>(p.ws_o + (base + j) * D + 4 * dq);
@@ -520,23 +520,10 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(AttnParams p
         *reinterpret_cast<uint2*>(p.out + ((size_t)(row0 + rr) * p.Hq + qh) * D + 4 * dq) = make_uint2(w0, w1);
       }
     };
-    float4 o0[CK];
-    float m0[CK], l0[CK];
-    {
-      const size_t base = ((size_t)s * p.decode_max_q * p.Hq + qh) * p.max_splits;   // row 0
-#pragma unroll
-      for (int c = 0; c < CK; ++c) {
-        const int j = min(c * PPI + sub, p.max_splits - 1);
-        m0[c] = p.ws_m[base + j];
-        l0[c] = p.ws_l[base + j];
-        o0[c] = *reinterpret_cast<const float4*>(p.ws_o + (base + j) * D + 4 * dq);
-      }
-    }
     const int nsplit = p.ws_nparts[(size_t)s * p.Hkv + qh / (p.Hq / p.Hkv)];
     const SeqInfo si = seq_info(p, s);
     if (si.tiles == 0 || nsplit <= 1) return;    // no decode rows, or written by the decode kernel
-    merge_row(0, nsplit, si.row0, o0, m0, l0);
-    for (int rr = 1; rr < si.q; ++rr) merge_row(rr, nsplit, si.row0, nullptr, nullptr, nullptr);
+    for (int rr = 0; rr < si.q; ++rr) merge_row(rr, nsplit, si.row0);
     return;
   }
   const SeqInfo si = seq_info(p, s);
