@@ -259,24 +259,23 @@ void decode_kernel(AttnParams p) {
     };
 
     const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
-    int bts[NBT];
-    load_bts(t_begin, bts);
-    uint4 kreg[NL], vreg[NL];
-    issue(kbase, knew_h, bts, kreg, t_begin);
-    issue(vbase, vnew_h, bts, vreg, t_begin);
-    for (int tile_i = 0; tile_i < ntiles; ++tile_i) {
+    // One tile: its K and V wait in kr / vr; as soon as each is in LDS the registers are
+    // refilled with tile tile_i + AHEAD, so AHEAD register sets keep AHEAD tiles in flight.
+    auto tile_step = [&](uint4* kr, uint4* vr, int tile_i, auto ahead_c) {
+      constexpr int AHEAD = decltype(ahead_c)::value;
       const int ts = t_begin + tile_i * kTile;
       const int nvalid = min(kTile, t_end - ts);
-      const bool has_next = tile_i + 1 < ntiles;
-      int bts_next[NBT];
+      const bool refill = tile_i + AHEAD < ntiles;
+      const int tn = ts + AHEAD * kTile;
+      int bts_n[NBT];
 #pragma unroll
-      for (int j = 0; j < NBT; ++j) bts_next[j] = 0;
-      if (has_next) load_bts(ts + kTile, bts_next);
+      for (int j = 0; j < NBT; ++j) bts_n[j] = 0;
+      if (refill) load_bts(tn, bts_n);
 
-      // ---- K tile -> LDS; refill the K registers with the next tile ----
-      stage(kreg, nvalid);
+      // ---- K tile -> LDS; refill the K registers with tile tile_i + AHEAD ----
+      stage(kr, nvalid);
       __builtin_amdgcn_sched_barrier(0);
-      if (has_next) issue(kbase, knew_h, bts_next, kreg, ts + kTile);
+      if (refill) issue(kbase, knew_h, bts_n, kr, tn);
       wave_lds_sync();
 
       // ---- S^T = K Q^T ----
@@ -293,10 +292,10 @@ void decode_kernel(AttnParams p) {
       }
       wave_lds_sync();                           // K reads done before V overwrites the buffer
 
-      // ---- V tile -> LDS; refill the V registers with the next tile ----
-      stage(vreg, nvalid);
+      // ---- V tile -> LDS; refill the V registers with tile tile_i + AHEAD ----
+      stage(vr, nvalid);
       __builtin_amdgcn_sched_barrier(0);
-      if (has_next) issue(vbase, vnew_h, bts_next, vreg, ts + kTile);
+      if (refill) issue(vbase, vnew_h, bts_n, vr, tn);
 
       // ---- online softmax for column n over this tile's tokens (exp2 domain) ----
       const int last = MULTI ? min(nvalid - 1, lim - ts) : nvalid - 1;   // last token column n sees
@@ -361,9 +360,15 @@ void decode_kernel(AttnParams p) {
         }
       }
       wave_lds_sync();                           // V reads done before the next K lands
-#pragma unroll
-      for (int j = 0; j < NBT; ++j) bts[j] = bts_next[j];
-    }
+    };
+    int bts[NBT];
+    load_bts(t_begin, bts);
+    // one register set: K and V run one tile ahead (for 8-bit pools a second set, two tiles
+    // ahead, measured slower: 69 -> 79 us per call on the Llama-3-8B batch)
+    uint4 kreg[NL], vreg[NL];
+    issue(kbase, knew_h, bts, kreg, t_begin);
+    issue(vbase, vnew_h, bts, vreg, t_begin);
+    for (int tile_i = 0; tile_i < ntiles; ++tile_i) tile_step(kreg, vreg, tile_i, IntC<1>());
 
     // ---- finish: lane (kg, n) holds dims db*16 + 4kg + i of column n ----
     // (the column's row and head are recomputed here rather than kept live through the loop)
