@@ -24,9 +24,10 @@
 //     KV heads, 64-token tile), in that order.  The grid has one wave per
 //     resident wave slot of the device; a workgroup holds one wave per KV head
 //     of a group (up to 8) and takes an equal consecutive share of units,
-//     walked as pieces of consecutive (sequence, group) segments.  The waves of a workgroup read the same slots for different
-//     heads, and a slot's heads sit side by side in the pool, so the DRAM rows
-//     behind each slot are read together.
+//     walked as pieces of consecutive (sequence, group) segments.  The waves
+//     of a workgroup read the same slots for different heads, and a slot's
+//     heads sit side by side in the pool, so the DRAM rows behind each slot
+//     are read together.
 //   * Loads are fully coalesced: 16 lanes read one 256-byte row (16 bytes each),
 //     4 rows per instruction; the pool block of each instruction is
 //     wave-uniform (scalar base).  K and V of a tile arrive in registers.
@@ -42,6 +43,9 @@
 //     rounded to bf16 in place; A = V^T.
 //   * Streaming: each register set is refilled with the next tile as soon as
 //     its contents are in LDS, so K and V both run one tile ahead.
+//   * Fused append: positions that are this call's new tokens are read from the
+//     new rows (k_new / v_new) instead of the pools, which the merge launch
+//     fills afterwards.
 //   A piece that covers its whole (sequence, head) writes bf16 output directly;
 //   otherwise fp32 partials (O, m, l) go to the workspace for the merge kernel.
 #include <algorithm>
