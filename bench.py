@@ -26,7 +26,8 @@ Prints ONE JSON line on stdout:
   separate_calls the same steps through kv_append + paged_attention;
   mixed         (mixed batch only) decode-only and prefill-only sub-batch times;
   append        kv_append alone at T = 64, 4288 and 65536 tokens (HBM GB/s);
-  measured_peaks a device copy and a bf16 GEMM through torch, for context;
+  measured_peaks a device copy and a bf16 GEMM through torch, and the library's
+                streaming-read and matrix-core-loop probes, for context;
   cpu_baseline  the float64 CPU oracle on a bounded sample of the same batch.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config i]
@@ -394,8 +395,26 @@ def measured_peaks(torch, dev, stream):
     b = torch.randn(n, n, device=dev).to(torch.bfloat16)
     ms = time_calls(lambda: torch.mm(a, b), 10, 3, stream, torch)
     tf = 2 * n ** 3 / (pct(ms, 50) * 1e-3) / 1e12
+    del a, b
+    # the library's own probes: a streaming read (the decode kernel's load) and a matrix-core loop
+    # (the prefill kernel's instruction) on all compute units
+    import paged_kv_cache_tables_amd as pkv
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    buf = torch.ones(2 << 30, dtype=torch.uint8, device=dev)
+    read_call = pkv.peak_read(buf, sink, stream=stream, prepare=True)
+    read_ms = region_ms(read_call, 5, 2, stream, torch)
+    read_gbs = buf.numel() / (read_ms * 1e-3) / 1e9
+    del read_call, buf
+    iters = 10000
+    flops = pkv.peak_mfma_bf16(iters, sink, stream=stream)
+    mfma_ms = region_ms(lambda: pkv.peak_mfma_bf16(iters, sink, stream=stream), 5, 1, stream, torch)
+    mfma_tf = flops / (mfma_ms * 1e-3) / 1e12
     return {"device_copy_GBps": round(copy_gbs, 1), "device_copy_note": "1 GiB copy, bytes read + written",
-            "bf16_gemm_TFLOPs": round(tf, 1), "bf16_gemm_note": "torch.mm 8192^3 bf16 (hipBLASLt)"}
+            "bf16_gemm_TFLOPs": round(tf, 1), "bf16_gemm_note": "torch.mm 8192^3 bf16 (hipBLASLt)",
+            "stream_read_GBps": round(read_gbs, 1),
+            "stream_read_note": "pkv_peak_read: 2 GiB read once with non-temporal 16-byte loads",
+            "mfma_bf16_TFLOPs": round(mfma_tf, 1),
+            "mfma_bf16_note": "pkv_peak_mfma_bf16: back-to-back 32x32x16 bf16 MFMAs, 2 waves per SIMD, no memory"}
 
 
 def main():
@@ -640,9 +659,13 @@ def main():
         result["measured_peaks"] = measured_peaks(torch, dev, stream)
         result["measured_peaks"]["decode_frac_of_device_copy"] = round(
             achieved / result["measured_peaks"]["device_copy_GBps"], 4)
+        result["measured_peaks"]["decode_frac_of_stream_read"] = round(
+            achieved / result["measured_peaks"]["stream_read_GBps"], 4)
         if "prefill" in result:
             result["measured_peaks"]["prefill_frac_of_bf16_gemm"] = round(
                 result["prefill"]["roofline"]["achieved"] / result["measured_peaks"]["bf16_gemm_TFLOPs"], 4)
+            result["measured_peaks"]["prefill_frac_of_mfma_loop"] = round(
+                result["prefill"]["roofline"]["achieved"] / result["measured_peaks"]["mfma_bf16_TFLOPs"], 4)
 
     if not args.no_cpu:
         import oracle

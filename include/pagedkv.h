@@ -376,6 +376,25 @@ PKV_API int32_t pkv_allocator_num_cached(const pkv_allocator* a);
 /* Human-readable name of a status code (static string). */
 PKV_API const char* pkv_status_string(int status);
 
+/*
+ * Measurement helpers (not part of the attention path): the device rates the
+ * attention kernels' figures are read against, measured on the GPU at hand.
+ *
+ * pkv_peak_read -- one streaming read of `bytes` (a multiple of 16) at `buf`
+ * (device, 16-byte aligned) with the non-temporal loads the decode kernel
+ * uses; `sink` is a device word that is never written in practice.  Time the
+ * call with events on `stream`: bytes / time is the read rate.
+ *
+ * pkv_peak_mfma_bf16 -- every wave of a two-waves-per-SIMD grid issues
+ * `iterations` x 8 independent v_mfma_f32_32x32x16_bf16 on register operands;
+ * *flops receives the floating-point operations the launch performs.
+ *
+ * Both return PKV_OK, PKV_EINVAL (bad pointer, size or count; nothing
+ * enqueued) or PKV_EHIP.
+ */
+PKV_API int pkv_peak_read(const void* buf, int64_t bytes, void* sink, void* stream);
+PKV_API int pkv_peak_mfma_bf16(int64_t iterations, void* sink, int64_t* flops, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

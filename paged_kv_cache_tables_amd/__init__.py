@@ -23,5 +23,7 @@ from ._lib import (  # noqa: F401
     paged_attention,
     paged_attention_append,
     paged_attention_fp8,
+    peak_mfma_bf16,
+    peak_read,
     workspace_bytes,
 )

@@ -89,6 +89,10 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_allocator_num_free.argtypes = [c_void_p]
     lib.pkv_allocator_num_cached.restype = c_int32
     lib.pkv_allocator_num_cached.argtypes = [c_void_p]
+    lib.pkv_peak_read.restype = c_int
+    lib.pkv_peak_read.argtypes = [c_void_p, c_int64, c_void_p, c_void_p]
+    lib.pkv_peak_mfma_bf16.restype = c_int
+    lib.pkv_peak_mfma_bf16.argtypes = [c_int64, c_void_p, i64p, c_void_p]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_status_string.argtypes = [c_int]
     _lib = lib
@@ -121,6 +125,29 @@ def _check(t, name, dtype, ndim=None, device=None):
         raise ValueError(f"{name} must be contiguous")
     if ndim is not None and t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def peak_read(buf, sink, stream=None, prepare=False):
+    """Measurement helper: one streaming read of the whole uint8 device tensor ``buf`` (size a
+    multiple of 16); ``sink`` a small int32 device tensor that is never written in practice."""
+    import torch
+    _check(buf, "buf", torch.uint8, 1, None)
+    _check(sink, "sink", torch.int32, 1, buf.device)
+    lib = load_library()
+    return _issue("pkv_peak_read", lib.pkv_peak_read,
+                  [buf.data_ptr(), buf.numel(), sink.data_ptr(), _stream_ptr(stream, buf.device)], prepare,
+                  (buf, sink))
+
+
+def peak_mfma_bf16(iterations: int, sink, stream=None):
+    """Measurement helper: a launch of back-to-back bf16 matrix-core products; returns its flops."""
+    import torch
+    _check(sink, "sink", torch.int32, 1, None)
+    flops = ctypes.c_int64(0)
+    lib = load_library()
+    _issue("pkv_peak_mfma_bf16", lib.pkv_peak_mfma_bf16,
+           [int(iterations), sink.data_ptr(), ctypes.byref(flops), _stream_ptr(stream, sink.device)], False)
+    return int(flops.value)
 
 
 _CARG = type(ctypes.byref(ctypes.c_int()))

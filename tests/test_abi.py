@@ -247,3 +247,14 @@ def test_paged_attention_append_checks_pointers_before_launch(lib):
         assert lib.paged_attention_append(*args) == PKV_EINVAL, field   # misaligned
     args = attn_append_args(workspace=FAKE, workspace_bytes=ctypes.byref(n), num_q_tokens=0)
     assert lib.paged_attention_append(*args) == PKV_OK                 # empty batch: no launch
+
+
+def test_peak_helpers_validate_before_launch(lib):
+    flops = ctypes.c_int64(0)
+    assert lib.pkv_peak_read(None, 1 << 20, FAKE, None) == PKV_EINVAL
+    assert lib.pkv_peak_read(FAKE, 1 << 20, None, None) == PKV_EINVAL
+    assert lib.pkv_peak_read(FAKE, 1000, FAKE, None) == PKV_EINVAL          # not a multiple of 16
+    assert lib.pkv_peak_read(FAKE + 8, 1 << 20, FAKE, None) == PKV_EINVAL   # misaligned
+    assert lib.pkv_peak_mfma_bf16(0, FAKE, ctypes.byref(flops), None) == PKV_EINVAL
+    assert lib.pkv_peak_mfma_bf16(10, None, ctypes.byref(flops), None) == PKV_EINVAL
+    assert lib.pkv_peak_mfma_bf16(10, FAKE, None, None) == PKV_EINVAL
