@@ -125,3 +125,46 @@ def test_fused_step_captured_in_hip_graph(gpu):
         torch.cuda.synchronize()
         assert np.array_equal(to_host_bits(db.out), want[i][0]), f"replay {rep} output differs"
         assert np.array_equal(to_host_bits(db.k_cache), want[i][1]), f"replay {rep} pool differs"
+
+
+def random_batch(seed):
+    """A seeded batch whose shape the fixed cases do not cover: KV-head counts that are not powers
+    of two (the decode workgroups then take 1 or 2 or 4 heads together), a random mix of rows per
+    sequence (none, one, a few, a long chunk) and, half of the time, a shared prefix."""
+    rng = np.random.default_rng(1000 + seed)
+    Hkv = int(rng.choice([1, 2, 3, 4, 6, 8, 12]))
+    G = int(rng.choice([g for g in (1, 2, 4, 8, 16) if Hkv * g <= 64]))
+    D = int(rng.choice([64, 128]))
+    bs = int(rng.choice([8, 16, 32]))
+    n = int(rng.integers(1, 40))
+    specs = []
+    for _ in range(n):
+        kind = rng.random()
+        if kind < 0.1:
+            L, q = int(rng.integers(1, 300)), 0
+        elif kind < 0.6:
+            L, q = int(rng.integers(1, 3000)), 1
+        elif kind < 0.8:
+            q = int(rng.integers(2, 9))
+            L = q + int(rng.integers(0, 2000))
+        else:
+            q = int(rng.integers(9, 300))
+            L = q + int(rng.integers(0, 1500))
+        specs.append((L, q))
+    share = None
+    if rng.random() < 0.5:
+        prefix = bs * int(rng.integers(1, 8))
+        sharers = [i for i, (L, q) in enumerate(specs) if L - q >= prefix]
+        if len(sharers) >= 2:
+            share = (set(sharers), prefix)
+    order = rng.permutation(n).tolist()
+    name = f"random-{seed}-hkv{Hkv}-g{G}-d{D}-bs{bs}-n{n}"
+    return W.custom(name, specs, Hkv * G, Hkv, D, bs, seed=seed, row_order=order, share=share)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_fused_and_separate_on_random_batches(seed):
+    wl = random_batch(seed)
+    if wl.num_q_tokens == 0:
+        pytest.skip("batch without rows")
+    check_fused_equals_separate(wl, wl.name)
