@@ -53,6 +53,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "planner.h"
 
 namespace pkv {
 
@@ -443,14 +444,25 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(AttnParams p
   constexpr int WPC = WIDE ? kMergeWaves : 1;    // waves per (sequence, query head)
   __shared__ float4 part[WIDE ? kMergeWaves : 1][LPP];
   __shared__ float lpart[WIDE ? kMergeWaves : 1];
-  if ((int)blockIdx.x >= p.merge_blocks) {       // fused append: scatter the new rows into the pools
+  // workgroups: [planner] merge cells ... [fused append ...]
+  int bid = (int)blockIdx.x;
+  if (p.plan_first) {
+    if (bid == 0) {                              // the prefill kernel's work list, before it runs
+      __shared__ int plan_bins[kPlanBins];
+      __shared__ int plan_wave_tot[kMergeWaves];
+      plan_prefill_items<kMergeWaves * kWave>(p, plan_bins, plan_wave_tot);
+      return;
+    }
+    bid -= 1;
+  }
+  if (bid >= p.merge_blocks) {                   // fused append: scatter the new rows into the pools
     // one thread per 16-byte chunk of a K or V row, grid-stride over the append workgroups
     const int row_chunks = p.Hkv * D / 8;
     const int64_t per_token = 2 * (int64_t)row_chunks;
     const int64_t total = p.num_q_tokens * per_token;
-    const int64_t nthreads = (int64_t)(gridDim.x - p.merge_blocks) * blockDim.x;
+    const int64_t nthreads = (int64_t)(gridDim.x - p.plan_first - p.merge_blocks) * blockDim.x;
     const int64_t num_slots = p.num_blocks * p.bs;
-    for (int64_t idx = (int64_t)(blockIdx.x - p.merge_blocks) * blockDim.x + threadIdx.x; idx < total;
+    for (int64_t idx = (int64_t)(bid - p.merge_blocks) * blockDim.x + threadIdx.x; idx < total;
          idx += nthreads) {
       const int64_t i = idx / per_token;
       const int rem = (int)(idx - i * per_token);
@@ -467,7 +479,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(AttnParams p
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = (int)(threadIdx.x / kWave);
   // cell = (sequence s, query head qh); its decode rows are merged one after the other
-  const int cell = WIDE ? (int)blockIdx.x : (int)blockIdx.x * kMergeWaves + wv;
+  const int cell = WIDE ? bid : bid * kMergeWaves + wv;
   if (cell >= p.num_seqs * p.Hq) return;         // uniform over the workgroup in the wide form
   const int s = cell / p.Hq, qh = cell % p.Hq;
   const int sub = lane / LPP, dq = lane % LPP;
@@ -653,7 +665,11 @@ hipError_t launch_merge(const AttnParams& p, hipStream_t stream) {
     const int64_t chunks = p.num_q_tokens * 2 * ((int64_t)p.Hkv * p.D / 8);
     append_blocks = std::min<int64_t>((chunks + kMergeWaves * kWave - 1) / (kMergeWaves * kWave), 4096);
   }
-  const dim3 grid((unsigned)(q.merge_blocks + append_blocks));
+  // the prefill planner rides along as the first workgroup when prefill rows are possible
+  q.plan_first = p.max_query_len > p.decode_max_q ? 1 : 0;
+  q.plan_bin_shift = 0;
+  while ((((int64_t)p.max_blocks * p.bs + 63) / 64 >> q.plan_bin_shift) >= kPlanBins) ++q.plan_bin_shift;
+  const dim3 grid((unsigned)(q.plan_first + q.merge_blocks + append_blocks));
   const dim3 block(kMergeWaves * kWave);
   if (p.D == 128) {
     if (wide) hipLaunchKernelGGL((merge_kernel<128, true>), grid, block, 0, stream, q);

@@ -41,7 +41,9 @@ struct AttnParams {
   const int64_t* slots;           // [num_q_tokens]; < 0 or >= num_blocks * bs: not stored
   uint4* k_pool;                  // the pools, writable
   uint4* v_pool;
-  int merge_blocks;               // merge launch: workgroups that merge (the rest append)
+  int merge_blocks;               // merge launch: workgroups that merge (then the append ones)
+  int plan_first;                 // merge launch: 1 if its first workgroup plans the prefill items
+  int plan_bin_shift;             // planner: tile counts >> this fit its buckets
   int2* plan_items;               // prefill work list (sequence, row tile), written by the planner
   int* plan_count;                // number of valid items
   int plan_capacity;              // items the workspace holds

@@ -40,10 +40,10 @@
 //     only rounding differs, and bf16 keeps its relative precision at any
 //     magnitude.  The row sums add the bf16 weights the MFMA multiplies (two
 //     per v_dot2_f32_bf16), so numerator and denominator see the same values.
-//   * A one-block planner kernel lists the (sequence, row tile) items of the
-//     prefill sequences in the workspace, longest first (most key tiles), so
-//     that no workgroup is launched for decode rows and the longest items do
-//     not start last; workgroup ids take the KV heads fastest, so with 8 KV
+//   * A planner (one workgroup of the merge launch, see planner.h) lists the
+//     (sequence, row tile) items of the prefill sequences in the workspace,
+//     longest first (most key tiles), so that no workgroup is launched for
+//     decode rows and the longest items do not start last; workgroup ids take the KV heads fastest, so with 8 KV
 //     heads each XCD runs one head's items and keeps its K/V rows in its L2.
 #include "common.h"
 #include "kernels.h"
@@ -64,76 +64,6 @@ typedef short short4v __attribute__((ext_vector_type(4)));
 typedef short short8v __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) short4v lds_short4;
 typedef __attribute__((address_space(3))) void lds_void;
-
-// Lists the prefill work items (sequence, row tile) of one call, longest first.  A
-// sequence with q_s > min_rows rows (fewer are computed as decode rows) has
-// ceil(q_s / rows_per_tile) row tiles; row tile mt needs the keys before position
-// L - q_s + min((mt + 1) rows_per_tile, q_s), i.e. that many keys / 64 tiles of work.
-// Workgroups start in id order as earlier ones finish, so listing the items by
-// decreasing work is the longest-processing-time-first schedule: the long items
-// (late row tiles of long prefixes) are not left to start last.  One block; a
-// counting sort over the items' tile counts (bucketed by >> bin_shift so that the
-// buckets fit in LDS), items of one bucket in any order.
-constexpr int kPlanThreads = 1024;
-constexpr int kPlanBins = 4096;
-
-__global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(const int32_t* __restrict__ qsl,
-                                                                    const int32_t* __restrict__ seq_lens, int num_seqs,
-                                                                    int max_len, int min_rows, int rows_per_tile,
-                                                                    int bin_shift, int2* __restrict__ items,
-                                                                    int* __restrict__ count, int capacity) {
-  __shared__ int bins[kPlanBins];                // counts, then the next free position of each bucket
-  __shared__ int wave_tot[kPlanThreads / kWave];
-  const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
-  for (int i = t; i < kPlanBins; i += kPlanThreads) bins[i] = 0;
-  __syncthreads();
-  // bucket of row tile mt of a sequence (q rows after prior cached keys): longest first
-  auto bucket = [&](int prior, int q, int mt) {
-    const int key_end = prior + min((mt + 1) * rows_per_tile, q);
-    const int tiles = (max(key_end, 1) + 63) / 64;
-    return kPlanBins - 1 - min(tiles >> bin_shift, kPlanBins - 1);
-  };
-  auto seq_tiles = [&](int s, int& prior, int& q) -> int {   // row tiles of sequence s
-    q = qsl[s + 1] - qsl[s];
-    prior = min(seq_lens[s], max_len) - q;
-    return q > min_rows ? (q + rows_per_tile - 1) / rows_per_tile : 0;
-  };
-  for (int s = t; s < num_seqs; s += kPlanThreads) {
-    int prior, q;
-    const int nt = seq_tiles(s, prior, q);
-    for (int mt = 0; mt < nt; ++mt) atomicAdd(&bins[bucket(prior, q, mt)], 1);
-  }
-  __syncthreads();
-  // exclusive scan of the bins: thread t owns bins [PER t, PER t + PER)
-  constexpr int PER = kPlanBins / kPlanThreads;
-  int own[PER], sum = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) { own[i] = bins[PER * t + i]; sum += own[i]; }
-  int incl = sum;
-#pragma unroll
-  for (int d = 1; d < kWave; d *= 2) {
-    const int y = __shfl_up(incl, d, kWave);
-    if (lane >= d) incl += y;
-  }
-  if (lane == kWave - 1) wave_tot[w] = incl;
-  __syncthreads();
-  int run = incl - sum;
-  for (int i = 0; i < w; ++i) run += wave_tot[i];
-  int total = 0;
-  for (int i = 0; i < kPlanThreads / kWave; ++i) total += wave_tot[i];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) { bins[PER * t + i] = run; run += own[i]; }
-  __syncthreads();
-  for (int s = t; s < num_seqs; s += kPlanThreads) {
-    int prior, q;
-    const int nt = seq_tiles(s, prior, q);
-    for (int mt = 0; mt < nt; ++mt) {
-      const int pos = atomicAdd(&bins[bucket(prior, q, mt)], 1);
-      if (pos < capacity) items[pos] = make_int2(s, mt);
-    }
-  }
-  if (t == 0) *count = min(total, capacity);
-}
 
 // s_waitcnt immediate that waits until at most N vector-memory operations of this wave are
 // outstanding (the other counters are left alone).
@@ -536,15 +466,8 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
 template <int D, bool F8>
 hipError_t dispatch_g(const AttnParams& p, hipStream_t stream) {
   const int G = p.Hq / p.Hkv;
-  const int rows = kPairsPerBlock / G;
-  const int max_len = p.max_blocks * p.bs;
-  int bin_shift = 0;
-  while ((((max_len + 63) / 64) >> bin_shift) >= kPlanBins) ++bin_shift;
-  hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, p.qsl, p.seq_lens, p.num_seqs,
-                     max_len, p.decode_max_q, rows, bin_shift, p.plan_items, p.plan_count, p.plan_capacity);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // one workgroup per (possible item, KV head)
+  // the work list was written by the planner workgroup of the merge launch; one workgroup
+  // per (possible item, KV head)
   dim3 grid((unsigned)((int64_t)p.Hkv * p.plan_stride));
   switch (G) {
     case 1: hipLaunchKernelGGL((prefill_kernel<D, 1, F8>), grid, dim3(kWavesP * kWave), 0, stream, p); break;
