@@ -222,7 +222,7 @@ def prefill_report(pkv, d, stream, torch):
                          "frac": round(tf / BF16_PEAK_TFLOPS, 4),
                          "timing": "HIP events around 20 back-to-back calls, / 20 (call_us_avg)",
                          "note": "flops = 4 d Hq x causal (row, key) pairs; the call also launches the "
-                                 "(empty) decode and merge grids and the planner"}}
+                                 "(empty) decode grid and the merge launch that carries the planner"}}
 
 
 def append_report(pkv, dev, torch, stream):
