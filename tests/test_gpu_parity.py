@@ -169,6 +169,21 @@ def test_edge_shapes(name, specs, Hq, Hkv, D, bs):
     run_and_check(wl)
 
 
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 0.75], ids=["negative", "zero", "large"])
+def test_any_finite_softmax_scale(scale):
+    """The softmax scale is any finite float: negative (the prefill kernel negates the
+    query instead, so that both paths take the row max of the scaled scores), zero (uniform
+    weights) and large (weights concentrated on a few keys, several rescales of the running
+    max), over decode rows, multi-row decode rows and prefill rows, d 128 and d 64."""
+    import dataclasses
+    for D in (128, 64):
+        wl = W.custom(f"scale-{scale}-d{D}", [(700, 1), (130, 3), (300, 300), (1500, 64), (9, 1), (2100, 1)],
+                      16, 4, D, 16, seed=D)
+        wl = dataclasses.replace(wl, scale=float(np.float32(scale)))
+        print(f"scale {wl.scale} d {D}", flush=True)
+        run_and_check(wl)
+
+
 def test_sequences_without_rows_and_interleaved_order():
     specs = [(40, 1), (25, 0), (300, 20), (9, 0), (1, 1), (200, 1)]
     wl = W.custom("zero-rows", specs, 8, 2, 128, 16, seed=3, row_order=[3, 0, 5, 2, 1, 4])
