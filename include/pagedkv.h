@@ -373,6 +373,47 @@ PKV_API int pkv_allocator_table(pkv_allocator* a, int64_t alloc_id, int32_t* blo
 PKV_API int32_t pkv_allocator_num_free(const pkv_allocator* a);
 PKV_API int32_t pkv_allocator_num_cached(const pkv_allocator* a);
 
+/*
+ * pkv_check_metadata -- checks one step's metadata on the device against the
+ * contract of kv_append and paged_attention (a debugging aid; the attention
+ * calls themselves never test it).  The relations are those of the block-table
+ * scheme ([TGI] "Under the Hood: PagedAttention": logical block i of a
+ * sequence lives in the physical block its table names, and a new token is
+ * stored at its position's slot) and of chunked prefill ([TGI] "Advanced
+ * Pattern: Chunked Prefill": the q_s rows of a sequence of L tokens are its
+ * positions L - q_s .. L - 1).
+ *
+ *   block_tables, seq_lens, query_start_loc, num_seqs, num_q_tokens,
+ *   max_blocks_per_seq, max_query_len, num_blocks, block_size
+ *                  as in paged_attention (device arrays, host scalars).
+ *   slot_mapping   device, int64 [num_q_tokens] -- the slots of this step's
+ *                  new tokens, row i being the token of query row i (the
+ *                  layout of paged_attention_append) -- or NULL to skip the
+ *                  slot checks.
+ *   error_word     device int32, written: cleared, then the OR of the flags
+ *                  below for every violation found (0: the contract holds).
+ *                  Read it after the stream reaches this point.
+ *   stream         hipStream_t.
+ *
+ * Not checked: that slots are distinct within a call and that no slot lies
+ * in a block shared with another sequence (both need the whole pool's
+ * ownership, which the allocator holds).  Returns PKV_OK, PKV_EINVAL (null
+ * error_word or query_start_loc, null tables or lengths with num_seqs > 0,
+ * negative sizes, block_size <= 0; nothing enqueued) or PKV_EHIP.
+ */
+#define PKV_META_QSL         0x01  /* query_start_loc[0] != 0, decreasing, or last != num_q_tokens */
+#define PKV_META_QUERY_LEN   0x02  /* some q_s > max_query_len                                  */
+#define PKV_META_LENGTH      0x04  /* some L < 0, or a sequence with rows has L < q_s            */
+#define PKV_META_TABLE_SPAN  0x08  /* some L > max_blocks_per_seq * block_size                    */
+#define PKV_META_TABLE_ENTRY 0x10  /* a needed table entry (block < ceil(L / bs)) outside [0, NB) */
+#define PKV_META_SLOT_RANGE  0x20  /* a row's slot >= num_blocks * block_size                      */
+#define PKV_META_SLOT_TABLE  0x40  /* a row's slot is not its position's slot under the table      */
+PKV_API int pkv_check_metadata(const int32_t* block_tables, const int32_t* seq_lens,
+                               const int32_t* query_start_loc, int32_t num_seqs, int64_t num_q_tokens,
+                               int32_t max_blocks_per_seq, int32_t max_query_len,
+                               const int64_t* slot_mapping, int64_t num_blocks, int32_t block_size,
+                               int32_t* error_word, void* stream);
+
 /* Human-readable name of a status code (static string). */
 PKV_API const char* pkv_status_string(int status);
 

@@ -3,17 +3,19 @@
 The work is done by the HIP library ``libpagedkv.so`` (C ABI in
 ``include/pagedkv.h``); this package is a thin ctypes binding with the same
 calls (the three of the bf16 cache, the append and attention of the 8-bit
-E4M3 cache, the block copy of copy-on-write) and the host block allocator
+E4M3 cache, the block copy of copy-on-write, the metadata check) and the host block allocator
 with its radix prefix cache, taking torch tensors for device memory and
 streams.  Importing
 the package does not load the library; the first call does, and fails loudly
 if it is missing (build it with ``python -m paged_kv_cache_tables_amd.build``).
 """
 from ._lib import (  # noqa: F401
+    META_FLAGS,
     AllocatorFull,
     BlockAllocator,
     PagedKVError,
     PreparedCall,
+    check_metadata,
     kv_copy_blocks,
     kv_append,
     kv_append_fp8,

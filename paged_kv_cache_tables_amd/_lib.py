@@ -93,6 +93,9 @@ def load_library() -> ctypes.CDLL:
     lib.pkv_peak_read.argtypes = [c_void_p, c_int64, c_void_p, c_void_p]
     lib.pkv_peak_mfma_bf16.restype = c_int
     lib.pkv_peak_mfma_bf16.argtypes = [c_int64, c_void_p, i64p, c_void_p]
+    lib.pkv_check_metadata.restype = c_int
+    lib.pkv_check_metadata.argtypes = [c_void_p, c_void_p, c_void_p, c_int32, c_int64, c_int32, c_int32,
+                                       c_void_p, c_int64, c_int32, c_void_p, c_void_p]
     lib.pkv_status_string.restype = ctypes.c_char_p
     lib.pkv_status_string.argtypes = [c_int]
     _lib = lib
@@ -390,6 +393,55 @@ def kv_copy_blocks(k_cache, v_cache, src, dst, stream=None) -> None:
                                        _stream_ptr(stream, dev))
     if st != 0:
         raise PagedKVError("kv_copy_blocks", st)
+
+
+# Flags of pkv_check_metadata (include/pagedkv.h), by bit.
+META_FLAGS = {
+    0x01: "query_start_loc: [0] != 0, decreasing, or last != num_q_tokens",
+    0x02: "a sequence has more rows than max_query_len",
+    0x04: "a length is negative, or smaller than its sequence's rows",
+    0x08: "a length exceeds max_blocks_per_seq * block_size",
+    0x10: "a needed block-table entry lies outside the pool",
+    0x20: "a slot lies outside the pool",
+    0x40: "a row's slot is not its position's slot under the block table",
+}
+
+
+def check_metadata(block_tables, seq_lens, query_start_loc, num_q_tokens, max_query_len, num_blocks,
+                   block_size, slot_mapping=None, error_word=None, stream=None):
+    """Device check of one step's metadata against the contract of kv_append and
+    paged_attention (pkv_check_metadata).  With ``error_word`` (an int32 device tensor of one
+    element) the check is only enqueued and None is returned; without it a one-element tensor
+    is allocated here, the stream synchronised and the flags returned (0: the contract holds;
+    see META_FLAGS)."""
+    import torch
+    dev = block_tables.device
+    _check(block_tables, "block_tables", torch.int32, 2, dev)
+    _check(seq_lens, "seq_lens", torch.int32, 1, dev)
+    _check(query_start_loc, "query_start_loc", torch.int32, 1, dev)
+    S, max_blocks = block_tables.shape
+    if seq_lens.shape[0] != S or query_start_loc.shape[0] != S + 1:
+        raise ValueError("block_tables, seq_lens and query_start_loc disagree on the number of sequences")
+    slots_ptr = None
+    if slot_mapping is not None:
+        _check(slot_mapping, "slot_mapping", torch.int64, 1, dev)
+        if slot_mapping.shape[0] != num_q_tokens:
+            raise ValueError("slot_mapping must have num_q_tokens entries")
+        slots_ptr = slot_mapping.data_ptr()
+    own = error_word is None
+    if own:
+        error_word = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(error_word, "error_word", torch.int32, 1, dev)
+    st = load_library().pkv_check_metadata(block_tables.data_ptr(), seq_lens.data_ptr(),
+                                           query_start_loc.data_ptr(), S, int(num_q_tokens), max_blocks,
+                                           int(max_query_len), slots_ptr, int(num_blocks), int(block_size),
+                                           error_word.data_ptr(), _stream_ptr(stream, dev))
+    if st != 0:
+        raise PagedKVError("pkv_check_metadata", st)
+    if not own:
+        return None
+    (torch.cuda.current_stream(dev) if stream is None else stream).synchronize()
+    return int(error_word.item())
 
 
 class AllocatorFull(RuntimeError):

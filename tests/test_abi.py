@@ -258,3 +258,19 @@ def test_peak_helpers_validate_before_launch(lib):
     assert lib.pkv_peak_mfma_bf16(0, FAKE, ctypes.byref(flops), None) == PKV_EINVAL
     assert lib.pkv_peak_mfma_bf16(10, None, ctypes.byref(flops), None) == PKV_EINVAL
     assert lib.pkv_peak_mfma_bf16(10, FAKE, None, None) == PKV_EINVAL
+
+
+def check_args(**over):
+    a = dict(bt=FAKE, sl=FAKE, qsl=FAKE, num_seqs=2, num_q_tokens=3, max_blocks=4, max_query_len=2,
+             slots=None, num_blocks=8, block_size=16, error_word=FAKE, stream=None)
+    a.update(over)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("over", [
+    dict(error_word=None), dict(qsl=None), dict(bt=None), dict(sl=None), dict(num_seqs=-1),
+    dict(num_q_tokens=-1), dict(max_query_len=-1), dict(num_blocks=-1), dict(block_size=0),
+    dict(max_blocks=0),
+])
+def test_check_metadata_validation(lib, over):
+    assert lib.pkv_check_metadata(*check_args(**over)) == PKV_EINVAL
