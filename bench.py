@@ -420,8 +420,8 @@ def measured_peaks(torch, dev, stream):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=1, help="workload: 0..4 (1 = Llama-3-8B decode)")
     ap.add_argument("--copies", type=int, default=3, help="device copies of the batch cycled per step")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
