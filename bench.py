@@ -194,7 +194,7 @@ def region_ms(fn, n, warm, stream, torch):
     return a.elapsed_time(b) / n
 
 
-def sub_attention_ms(pkv, d, sub, scale, stream, torch, n=20):
+def sub_attention_ms(pkv, d, sub, scale, stream, torch, n=100):
     """paged_attention over a sub-batch (its own output and workspace): (per-call times with an
     event pair around each call, average over n back-to-back calls)."""
     wl = d.wl
@@ -204,7 +204,7 @@ def sub_attention_ms(pkv, d, sub, scale, stream, torch, n=20):
                      dtype=torch.uint8, device=d.dev)
     call = pkv.paged_attention(out, sub["q"], d.t["kc"], d.t["vc"], sub["bt"], sub["sl"], sub["qsl"], scale,
                                sub["max_query_len"], workspace=ws, stream=stream, prepare=True)
-    return time_calls(call, n, 3, stream, torch), region_ms(call, n, 2, stream, torch)
+    return time_calls(call, 30, 3, stream, torch), region_ms(call, n, 10, stream, torch)
 
 
 def prefill_report(pkv, d, stream, torch):
@@ -220,7 +220,7 @@ def prefill_report(pkv, d, stream, torch):
             "call_us_p10": round(pct(ms, 10) * 1e3, 3), "call_us_p90": round(pct(ms, 90) * 1e3, 3),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tf / BF16_PEAK_TFLOPS, 4),
-                         "timing": "HIP events around 20 back-to-back calls, / 20 (call_us_avg)",
+                         "timing": "HIP events around 100 back-to-back calls after 10 untimed ones, / 100 (call_us_avg)",
                          "note": "flops = 4 d Hq x causal (row, key) pairs; the call also launches the "
                                  "(empty) decode grid and the merge launch that carries the planner"}}
 
