@@ -3,7 +3,8 @@
     python -m paged_kv_cache_tables_amd.build
 
 Every source is compiled by hipcc for --offload-arch=gfx950 with packed-FP32
-instruction generation disabled.
+instruction generation disabled, one object per source (in parallel, under
+_build/), then linked into the shared library.
 """
 from __future__ import annotations
 
@@ -11,6 +12,7 @@ import glob
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -22,7 +24,6 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     "-Wno-unused-result",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -34,12 +35,7 @@ def sources():
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
-def build(verbose: bool = True, extra_flags=()) -> str:
-    srcs = sources()
-    cmd = [HIPCC, *FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc"),
-           *srcs, "-o", LIB + ".tmp"]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd, verbose):
     res = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 feature and says so; that is harmless
     noise = "is not a recognized feature for this target"
@@ -47,7 +43,30 @@ def build(verbose: bool = True, extra_flags=()) -> str:
     if msgs and verbose:
         print("\n".join(msgs), flush=True)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode})")
+        raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}")
+
+
+def build(verbose: bool = True, extra_flags=(), jobs: int = 0) -> str:
+    """Compile every source to an object (in parallel), then link the shared library."""
+    srcs = sources()
+    objdir = os.path.join(PKG, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(PKG, "csrc")]
+    cmds, objs = [], []
+    for src in srcs:
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        objs.append(obj)
+        cmds.append([HIPCC, *FLAGS, *extra_flags, *inc, "-c", src, "-o", obj])
+    if verbose:
+        for c in cmds:
+            print(" ".join(c), flush=True)
+    jobs = jobs or min(len(cmds), max(1, min(16, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"]
+    if verbose:
+        print(" ".join(link), flush=True)
+    _run(link, verbose)
     os.replace(LIB + ".tmp", LIB)
     return LIB
 
