@@ -33,28 +33,6 @@ int decode_rows(int Hq, int Hkv, int max_query_len) {
   return std::max(1, std::min(by_columns, max_query_len));
 }
 
-// Split-K partials of decode rows and their piece counts, then the prefill planner's
-// count and work list.  Depends only on (num_seqs, Hq, Hkv, D, max_blocks, bs,
-// max_query_len), so a caller can size it once.  A decode wave's share is at least
-// kMinShareTokens keys, so a (sequence, head) of at most max_blocks * bs keys is cut
-// into at most ceil(max_tokens / kMinShareTokens) + 1 pieces.
-WsLayout workspace_layout(int num_seqs, int Hq, int Hkv, int D, int max_blocks, int bs, int max_query_len) {
-  WsLayout w{};
-  const int64_t max_tokens = (int64_t)max_blocks * bs;
-  w.max_splits = (max_tokens + kMinShareTokens - 1) / kMinShareTokens + 1;
-  const int rows = pkv::kPrefillPairs / (Hq / Hkv);
-  w.plan_capacity = (int64_t)num_seqs * ((max_tokens + rows - 1) / rows);
-  const size_t cells = (size_t)num_seqs * decode_rows(Hq, Hkv, max_query_len) * Hq * w.max_splits;
-  w.o_off = 0;
-  w.m_off = round_up(cells * D * sizeof(float), 256);
-  w.l_off = w.m_off + round_up(cells * sizeof(float), 256);
-  w.nparts_off = w.l_off + round_up(cells * sizeof(float), 256);
-  w.count_off = w.nparts_off + round_up((size_t)num_seqs * Hkv * sizeof(int), 256);
-  w.items_off = w.count_off + 256;
-  w.total = w.items_off + round_up((size_t)w.plan_capacity * 8, 256);
-  return w;
-}
-
 // Decode waves of one call: the device's compute units times the resident waves per unit,
 // looked up once per device.
 int decode_waves_for_current_device() {
@@ -71,6 +49,30 @@ int decode_waves_for_current_device() {
   const int waves = cus * kDecodeWavesPerCU;
   if (dev >= 0) cached[dev].store(waves, std::memory_order_relaxed);
   return waves;
+}
+
+// Split-K partials of decode rows and the pieces' records, then the prefill planner's
+// count and work list.  A decode workgroup leaves at most two partial pieces (the first
+// and the last of its share), each a row of 16 columns per wave, so the partials take
+// decode_waves x 2 x 16 rows of D + 2 floats whatever the batch.  The rest depends on
+// (num_seqs, Hq, Hkv, max_blocks, bs).  A decode wave's share is at least kMinShareTokens
+// keys, so a (sequence, head) of at most max_blocks * bs keys is cut into at most
+// ceil(max_tokens / kMinShareTokens) + 1 pieces (max_splits; it picks the merge form).
+WsLayout workspace_layout(int num_seqs, int Hq, int Hkv, int D, int max_blocks, int bs, int decode_waves) {
+  WsLayout w{};
+  const int64_t max_tokens = (int64_t)max_blocks * bs;
+  w.max_splits = (max_tokens + kMinShareTokens - 1) / kMinShareTokens + 1;
+  const int rows = pkv::kPrefillPairs / (Hq / Hkv);
+  w.plan_capacity = (int64_t)num_seqs * ((max_tokens + rows - 1) / rows);
+  const size_t cells = (size_t)decode_waves * 2 * 16;
+  w.o_off = 0;
+  w.m_off = round_up(cells * D * sizeof(float), 256);
+  w.l_off = w.m_off + round_up(cells * sizeof(float), 256);
+  w.nparts_off = w.l_off + round_up(cells * sizeof(float), 256);
+  w.count_off = w.nparts_off + round_up((size_t)num_seqs * Hkv * 2 * sizeof(int), 256);
+  w.items_off = w.count_off + 256;
+  w.total = w.items_off + round_up((size_t)w.plan_capacity * 8, 256);
+  return w;
 }
 
 }  // namespace
@@ -178,8 +180,9 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
   if (!pkv::decode_supported(head_dim, G, block_size, fp8) || !pkv::prefill_supported(head_dim, G, block_size, fp8))
     return PKV_EUNSUPPORTED;
   if (num_seqs > 65535 || num_q_heads > 65535) return PKV_EUNSUPPORTED;   // 16-bit sequence and head counts
+  const int decode_waves = decode_waves_for_current_device();
   const WsLayout ws = workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
-                                       block_size, max_query_len);
+                                       block_size, decode_waves);
   if (ws.max_splits > 65535 || ws.plan_capacity > INT32_MAX) return PKV_EUNSUPPORTED;
   // decode work units (sequence, KV head, 64-token tile) are counted in 32 bits
   if ((int64_t)num_seqs * num_kv_heads * (((int64_t)max_blocks_per_seq * block_size + 63) / 64) > INT32_MAX)
@@ -228,7 +231,7 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
     p.k_pool = (uint4*)k_cache;
     p.v_pool = (uint4*)v_cache;
   }
-  p.decode_waves = decode_waves_for_current_device();
+  p.decode_waves = decode_waves;
   // the KV heads a decode workgroup reads together: the largest power of two <= 8 dividing Hkv
   p.decode_group = 1;
   while (p.decode_group < pkv::kMaxDecodeGroup && num_kv_heads % (2 * p.decode_group) == 0) p.decode_group *= 2;
@@ -239,7 +242,7 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
   p.ws_o = (float*)(wsb + ws.o_off);
   p.ws_m = (float*)(wsb + ws.m_off);
   p.ws_l = (float*)(wsb + ws.l_off);
-  p.ws_nparts = (int*)(wsb + ws.nparts_off);
+  p.ws_nparts = (int2*)(wsb + ws.nparts_off);
   p.plan_count = (int*)(wsb + ws.count_off);
   p.plan_items = (int2*)(wsb + ws.items_off);
   p.plan_capacity = (int)ws.plan_capacity;

@@ -29,6 +29,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// fp32 value rounded to the nearest bf16 (ties to even), returned as fp32.
+__device__ __forceinline__ float round_bf16(float f) { return (float)(__bf16)f; }
+
 // Two packed bf16 products accumulated in fp32: a.lo*b.lo + a.hi*b.hi + c.
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b),
@@ -67,15 +70,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load_stream16(const void* ptr) {
   const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
   return make_uint4(t.x, t.y, t.z, t.w);
-}
-
-// Load of a value that no kernel of the call writes (block tables, lengths), at a
-// wave-uniform address, through the scalar cache: the constant address space lets
-// the compiler use s_load instead of a vector load (which would share vmcnt with
-// the data loads in flight).
-template <typename T>
-__device__ __forceinline__ T load_invariant(const T* ptr) {
-  return *(const __attribute__((address_space(4))) T*)ptr;
 }
 
 // XOR swizzle of the 16-byte chunks of a row-major LDS tile with CH chunks per row

@@ -40,7 +40,7 @@
 //     accumulator column is one head: the per-head max and sum need a local
 //     reduction plus two lane exchanges.
 //   * Output transposed, O^T = V^T P^T: B = P^T is the score accumulator
-//     rounded to bf16 in place; A = V^T.
+//     rounded to bf16 in place (the row sum adds the same rounded weights); A = V^T.
 //   * Streaming: each register set is refilled with the next tile as soon as
 //     its contents are in LDS, so K and V both run one tile ahead.
 //   * Fused append: positions that are this call's new tokens are read from the
@@ -321,12 +321,14 @@ void decode_kernel(AttnParams p) {
       const float m_use = (MULTI && mn == -INFINITY) ? 0.f : mn;
       const float alpha = fast_exp2(m_run - m_use);   // 0 until the column's first visible key
       m_run = mn;
+      // the weights are rounded to bf16 here, once: the row sum adds exactly the values the
+      // PV product multiplies, so numerator and denominator see the same weights
       float psum = 0.f;
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float e = fast_exp2(sacc[tb][i] - m_use);   // 0 for masked tokens
+          const float e = round_bf16(fast_exp2(sacc[tb][i] - m_use));   // 0 for masked tokens
           sacc[tb][i] = e;
           psum += e;
         }
@@ -382,7 +384,10 @@ void decode_kernel(AttnParams p) {
     const int rr_e = n_e / G, g_e = n_e % G;
     const int first_w = a / share;                 // the workgroup holding tile 0 of (s, h)
     const int nseg = (a + nt - 1) / share - first_w + 1;   // pieces of (s, h)
-    if (tb0 == 0 && lane == 0) p.ws_nparts[(size_t)s * Hkv + h] = nseg;
+    // partial slot: 2 w for the piece that opens this workgroup's share, 2 w + 1 for a later one
+    // (only the last piece of a share can be a later partial one)
+    const int slot = 2 * w + (a + tb0 != x0 ? 1 : 0);
+    if (tb0 == 0 && lane == 0) p.ws_nparts[(size_t)s * Hkv + h] = make_int2(slot, nseg);
     float l_tot = l_part + __shfl_xor(l_part, 16, kWave);
     l_tot += __shfl_xor(l_tot, 32, kWave);
     if (rr_e < cur_q) {
@@ -396,9 +401,8 @@ void decode_kernel(AttnParams p) {
           const uint32_t w1 = (uint32_t)f32_to_bf16_rne(oacc[db][2] * inv) | ((uint32_t)f32_to_bf16_rne(oacc[db][3] * inv) << 16);
           *reinterpret_cast<uint2*>(op + db * 16 + 4 * kg_e) = make_uint2(w0, w1);
         }
-      } else {                                   // partial j = this wave's index among the pieces
-        const int j = w - first_w;
-        const size_t idx = (((size_t)s * p.decode_max_q + rr_e) * Hq + qh) * p.max_splits + j;
+      } else {                                   // a partial: row (slot, wave, column) of the workspace
+        const size_t idx = ((size_t)slot * WPG + wv) * 16 + n_e;
         const float vs = F8 ? p.v_scale : 1.f;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -483,13 +487,26 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(AttnParams p
   if (cell >= p.num_seqs * p.Hq) return;         // uniform over the workgroup in the wide form
   const int s = cell / p.Hq, qh = cell % p.Hq;
   const int sub = lane / LPP, dq = lane % LPP;
+  // the cell's KV head h, its wave in the decode workgroup and its column g of the group
+  const int G = p.Hq / p.Hkv, h = qh / G, g = qh % G, wv_h = h % p.decode_group;
+  // (the piece record is loaded together with the lengths; it is used only for sequences with
+  // decode rows, whose records the decode kernel wrote)
+  const int2 np = p.ws_nparts[(size_t)s * p.Hkv + h];
+  const SeqInfo si = seq_info(p, s);
+  const int nsplit = np.y;
+  // first row of piece j's 16-column block for each wave: piece 0 in slot np.x, piece j > 0 in
+  // slot 0 of the j-th following workgroup
+  auto piece_row = [&](int j) -> size_t {
+    const int slot = j == 0 ? np.x : 2 * (np.x / 2 + j);
+    return (size_t)slot * p.decode_group * 16;
+  };
   if constexpr (!WIDE) {
     // One pass with a running max, CK wave-wide steps (PPI pieces each) of loads in flight
     // at a time; lanes past the piece count load nothing and are discarded by selection,
     // never by a zero weight.
     constexpr int CK = 4;
     auto merge_row = [&](int rr, int nsplit, int row0) {
-      const size_t base = (((size_t)s * p.decode_max_q + rr) * p.Hq + qh) * p.max_splits;
+      const size_t col = (size_t)wv_h * 16 + rr * G + g;   // (wave, column) of this row's head
       float M = -INFINITY, ls = 0.f;
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
       for (int j0 = 0; j0 < nsplit; j0 += CK * PPI) {
@@ -502,9 +519,10 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(AttnParams p
           lj[c] = 0.f;
           o[c] = make_float4(0.f, 0.f, 0.f, 0.f);
           if (j < nsplit) {                      // only the pieces that exist are read
-            mj[c] = p.ws_m[base + j];
-            lj[c] = p.ws_l[base + j];
-            o[c] = *reinterpret_cast<const float4*>(p.ws_o + (base + j) * D + 4 * dq);
+            const size_t r = piece_row(j) + col;
+            mj[c] = p.ws_m[r];
+            lj[c] = p.ws_l[r];
+            o[c] = *reinterpret_cast<const float4*>(p.ws_o + r * D + 4 * dq);
           }
         }
         float mx = -INFINITY;
@@ -541,33 +559,29 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(AttnParams p
         *reinterpret_cast<uint2*>(p.out + ((size_t)(row0 + rr) * p.Hq + qh) * D + 4 * dq) = make_uint2(w0, w1);
       }
     };
-    const int nsplit = p.ws_nparts[(size_t)s * p.Hkv + qh / (p.Hq / p.Hkv)];
-    const SeqInfo si = seq_info(p, s);
     if (si.tiles == 0 || nsplit <= 1) return;    // no decode rows, or written by the decode kernel
     for (int rr = 0; rr < si.q; ++rr) merge_row(rr, nsplit, si.row0);
     return;
   }
-  const SeqInfo si = seq_info(p, s);
-  if (si.tiles == 0) return;                     // no decode rows (or nothing to attend)
-  const int nsplit = p.ws_nparts[(size_t)s * p.Hkv + qh / (p.Hq / p.Hkv)];
-  if (nsplit <= 1) return;                       // written directly by the decode kernel
+  if (si.tiles == 0 || nsplit <= 1) return;      // no decode rows, or written by the decode kernel
   const int w_in = WIDE ? wv : 0;
 
   for (int rr = 0; rr < si.q; ++rr) {
-    const size_t base = (((size_t)s * p.decode_max_q + rr) * p.Hq + qh) * p.max_splits;
+    const size_t col = (size_t)wv_h * 16 + rr * G + g;
     float M = -INFINITY;                         // every wave of the cell finds the same M
-    for (int j = lane; j < nsplit; j += kWave) M = fmaxf(M, p.ws_m[base + j]);
+    for (int j = lane; j < nsplit; j += kWave) M = fmaxf(M, p.ws_m[piece_row(j) + col]);
     M = wave_max(M);
 
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float ls = 0.f;
 #pragma unroll 4
     for (int j = w_in * PPI + sub; j < nsplit; j += WPC * PPI) {
-      const float f = fast_exp2(p.ws_m[base + j] - M);   // 0 for a piece that saw no key of this row
-      const float4 o = *reinterpret_cast<const float4*>(p.ws_o + (base + j) * D + 4 * dq);
+      const size_t r = piece_row(j) + col;
+      const float f = fast_exp2(p.ws_m[r] - M);   // 0 for a piece that saw no key of this row
+      const float4 o = *reinterpret_cast<const float4*>(p.ws_o + r * D + 4 * dq);
       acc.x = fmaf(f, o.x, acc.x); acc.y = fmaf(f, o.y, acc.y);
       acc.z = fmaf(f, o.z, acc.z); acc.w = fmaf(f, o.w, acc.w);
-      ls = fmaf(f, p.ws_l[base + j], ls);
+      ls = fmaf(f, p.ws_l[r], ls);
     }
 #pragma unroll
     for (int off = LPP; off < kWave; off *= 2) {

@@ -28,11 +28,17 @@ struct AttnParams {
   int decode_group;               // decode waves per workgroup: the KV heads taken together (divides Hkv)
   int decode_max_q;               // sequences with 1 <= q_s <= this are decode rows (q_s x G <= 16)
   int min_share_tiles;            // smallest share of 64-token tiles a decode wave takes
-  int max_splits;                 // pieces one (sequence, head) can be cut into: bounds the partials
-  float* ws_o;                    // [num_seqs, decode_max_q, Hq, max_splits, D]  unnormalised partials
-  float* ws_m;                    // [num_seqs, decode_max_q, Hq, max_splits]     partial max (exp2 domain)
-  float* ws_l;                    // [num_seqs, decode_max_q, Hq, max_splits]     partial sum of exponentials
-  int* ws_nparts;                 // [num_seqs, Hkv]                pieces of each decode (sequence, head)
+  int max_splits;                 // pieces one (sequence, head) can be cut into (picks the merge form)
+  // Partials of the pieces that do not cover their whole (sequence, head): a decode
+  // workgroup leaves at most two, the first and the last piece of its share (slots 0 and
+  // 1), each with one row of 16 columns per wave.  Partial row of (slot P = 2 workgroup +
+  // slot, wave v, column n): ((P * decode_group + v) * 16 + n).
+  float* ws_o;                    // [decode_waves * 2 * 16, D]  unnormalised partials
+  float* ws_m;                    // [decode_waves * 2 * 16]     partial max (exp2 domain)
+  float* ws_l;                    // [decode_waves * 2 * 16]     partial sum of exponentials
+  int2* ws_nparts;                // [num_seqs, Hkv]  (slot of the first piece, piece count) of each
+                                  // decode (sequence, KV head); later pieces sit in slot 0 of the
+                                  // following workgroups
   // fused append (paged_attention_append; null k_new otherwise): row i of k_new / v_new is the
   // new token of query row i, stored at slot slots[i].  Decode rows read this step's tokens
   // from k_new / v_new; the merge launch scatters every row into the pools afterwards.

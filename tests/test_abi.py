@@ -90,15 +90,20 @@ def attn_args(**over):
 def test_workspace_query_and_size(lib):
     n = ctypes.c_size_t(0)
     assert lib.paged_attention(*attn_args(workspace_bytes=ctypes.byref(n))) == PKV_OK
-    # 4 seqs x 4 heads x 1 split x (64 + 2) floats, each array 256-byte aligned
-    assert n.value >= 4 * 4 * 1 * 66 * 4
+    # decode partials: 2 slots of 16 columns of (64 + 2) floats per decode wave (2048 waves on a
+    # 256-CU device, also the figure without a device), each array 256-byte aligned
+    assert n.value >= 2048 * 2 * 16 * 66 * 4
     small = ctypes.c_size_t(n.value - 1)
     assert lib.paged_attention(*attn_args(workspace=FAKE, workspace_bytes=ctypes.byref(small))) == PKV_EWORKSPACE
     assert pkv.workspace_bytes(4, 4, 2, 64, 4, 16, max_query_len=5) == n.value
-    # decode-row partials: one row slot per sequence at max_query_len 1, up to 16 / G
-    assert pkv.workspace_bytes(4, 4, 2, 64, 4, 16, max_query_len=1) < n.value
-    assert pkv.workspace_bytes(4, 4, 2, 64, 4, 16, max_query_len=500) == \
-        pkv.workspace_bytes(4, 4, 2, 64, 4, 16, max_query_len=8)
+    # the partials do not depend on the batch: only the piece records and the prefill work
+    # list grow with the sequences and their length
+    assert pkv.workspace_bytes(4, 4, 2, 64, 4, 16, max_query_len=1) == n.value
+    assert pkv.workspace_bytes(4, 4, 2, 64, 4, 16, max_query_len=500) == n.value
+    assert pkv.workspace_bytes(400, 4, 2, 64, 4, 16) > n.value
+    assert pkv.workspace_bytes(4, 4, 2, 64, 4000, 16) > n.value
+    # D 128: 34 MB of partials for any batch
+    assert pkv.workspace_bytes(256, 64, 8, 128, 512, 16) < 40 << 20
 
 
 @pytest.mark.parametrize("over,expect", [
@@ -130,7 +135,7 @@ def test_paged_attention_checks_pointers_before_launch(lib):
 
 
 def test_status_strings(lib):
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert lib.pkv_status_string(code).decode() == _lib.STATUS[code]
 
 
