@@ -245,10 +245,16 @@ def _attention_shapes(name, out, q, k_cache, v_cache, block_tables, seq_lens, qu
     return NB, bs, Hkv, D, T, Hq, S, block_tables.shape[1], dev
 
 
-def _workspace(name, need, workspace, dev):
+def _workspace(name, need, workspace, dev, stream=None):
+    """The caller's workspace (checked), or a fresh one.  A fresh workspace comes from torch's
+    caching allocator on the current stream; when the call runs on another stream it is
+    recorded on that stream too, so that its memory is not handed out again before the
+    kernels that use it there have finished."""
     import torch
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        if stream is not None and stream != torch.cuda.current_stream(dev):
+            workspace.record_stream(stream)
     else:
         _check(workspace, "workspace", torch.uint8, 1, dev)
     return workspace
@@ -273,7 +279,7 @@ def paged_attention(out, q, k_cache, v_cache, block_tables, seq_lens, query_star
                              Hq, Hkv, D, NB, bs, float(scale), None, ctypes.byref(need), None)
     if st != 0:
         raise PagedKVError("paged_attention", st)
-    workspace = _workspace("paged_attention", need.value, workspace, dev)
+    workspace = _workspace("paged_attention", need.value, workspace, dev, stream)
     have = ctypes.c_size_t(workspace.numel())
     return _issue("paged_attention", lib.paged_attention,
                   [out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),
@@ -303,7 +309,7 @@ def paged_attention_append(out, q, k_new, v_new, slot_mapping, k_cache, v_cache,
                              Hq, Hkv, D, NB, bs, float(scale), None, ctypes.byref(need), None)
     if st != 0:
         raise PagedKVError("paged_attention_append", st)
-    workspace = _workspace("paged_attention_append", need.value, workspace, dev)
+    workspace = _workspace("paged_attention_append", need.value, workspace, dev, stream)
     have = ctypes.c_size_t(workspace.numel())
     return _issue("paged_attention_append", lib.paged_attention_append,
                   [out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(),
@@ -363,7 +369,7 @@ def paged_attention_fp8(out, q, k_cache, v_cache, block_tables, seq_lens, query_
                                  ctypes.byref(need), None)
     if st != 0:
         raise PagedKVError("paged_attention_fp8", st)
-    workspace = _workspace("paged_attention_fp8", need.value, workspace, dev)
+    workspace = _workspace("paged_attention_fp8", need.value, workspace, dev, stream)
     have = ctypes.c_size_t(workspace.numel())
     return _issue("paged_attention_fp8", lib.paged_attention_fp8,
                   [out.data_ptr(), q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(),

@@ -4,8 +4,12 @@ from __future__ import annotations
 
 import numpy as np
 
-TOL_MAX_ABS = 1e-2      # per element, raised to one bf16 ulp of the reference where that is larger
+TOL_MAX_ABS = 1e-2      # per element
 TOL_MEAN_ABS = 1e-3
+
+# Error statistics of every comparison made in this process, in order (printed as JSON lines
+# at the end of the session by conftest.py).
+PARITY_LOG: list = []
 
 
 def to_dev(arr: np.ndarray, dtype, device="cuda:0"):
@@ -65,7 +69,12 @@ def bf16_ulp(x: np.ndarray) -> np.ndarray:
 
 
 def compare(out_bits: np.ndarray, ref: np.ndarray, rows=None, label=""):
-    """Assert parity; return the error statistics.  `rows`: global rows to check (None = all)."""
+    """Assert parity; return the error statistics.  `rows`: global rows to check (None = all).
+
+    Every element must be within 1e-2 of the float64 reference, except where the bf16 output
+    cannot get that close at all: an element whose correctly rounded value |ref - rne(ref)|
+    itself exceeds 1e-2 (|ref| >= 4, where half a bf16 ulp is at least 1/64) may be off by one
+    bf16 ulp of the reference instead.  The mean absolute error must be <= 1e-3."""
     if rows is not None:
         rows = np.asarray(sorted(rows))
         out_bits = out_bits[rows]
@@ -74,10 +83,15 @@ def compare(out_bits: np.ndarray, ref: np.ndarray, rows=None, label=""):
     assert np.isfinite(ref).all(), "reference has NaN in the checked rows"
     err = np.abs(got - ref)
     floor = np.abs(ref - bf16_to_f64(_rne(ref)))
-    allowed = np.maximum(TOL_MAX_ABS, bf16_ulp(ref))
+    relaxed = floor > TOL_MAX_ABS
+    allowed = np.where(relaxed, bf16_ulp(ref), TOL_MAX_ABS)
     stats = dict(label=label, n=int(err.size), max_abs=float(err.max()), mean_abs=float(err.mean()),
-                 rounding_floor_max=float(floor.max()), n_ref_ge_4=int((np.abs(ref) >= 4).sum()),
+                 rounding_floor_max=float(floor.max()), rounding_floor_mean=float(floor.mean()),
+                 n_ref_ge_2=int((np.abs(ref) >= 2).sum()), n_ref_ge_4=int((np.abs(ref) >= 4).sum()),
+                 n_relaxed=int(relaxed.sum()),
+                 max_abs_strict=float(err[~relaxed].max()) if (~relaxed).any() else 0.0,
                  nonfinite=int((~np.isfinite(got)).sum()))
+    PARITY_LOG.append(stats)
     print("parity", stats, flush=True)
     assert stats["nonfinite"] == 0, stats
     bad = err > allowed

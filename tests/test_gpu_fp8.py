@@ -78,23 +78,6 @@ def run_and_check(wl, f8=None, rows=None, label=""):
     return compare(to_host_bits(db.out), ref, rows=rows, label=label or wl.name)
 
 
-def sampled_rows(wl, n_decode=64, per_prefill=16, seed=0):
-    rng = np.random.default_rng(seed)
-    qsl = wl.query_start_loc
-    rows = []
-    dec = []
-    for s in range(wl.num_seqs):
-        a, b = int(qsl[s]), int(qsl[s + 1])
-        if b - a == 1:
-            dec.append(a)
-        elif b - a > 1:
-            q = b - a
-            pick = {0, q - 1, q // 2} | set(rng.choice(q, size=min(per_prefill, q), replace=False).tolist())
-            rows.extend(a + j for j in sorted(pick))
-    rows.extend(rng.choice(dec, size=min(n_decode, len(dec)), replace=False).tolist() if dec else [])
-    return sorted(rows)
-
-
 # ---------------------------------------------------------------------------
 # append: codes bit-exact over the whole pool
 # ---------------------------------------------------------------------------
@@ -183,14 +166,12 @@ def test_fp8_config1_decode_all_rows():
     run_and_check(W.config1())
 
 
-def test_fp8_config2_decode_sampled_rows():
-    wl = W.config2()
-    run_and_check(wl, rows=sampled_rows(wl))
+def test_fp8_config2_decode_all_rows():
+    run_and_check(W.config2())
 
 
-def test_fp8_config3_mixed_sampled_rows():
-    wl = W.config3()
-    run_and_check(wl, rows=sampled_rows(wl, per_prefill=20))
+def test_fp8_config3_mixed_all_rows():
+    run_and_check(W.config3())
 
 
 def test_fp8_config4_long_context_all_rows():

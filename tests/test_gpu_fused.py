@@ -52,12 +52,7 @@ def check_fused_equals_separate(wl, label, oracle_rows="all"):
 
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
 def test_fused_equals_separate_calls(cfg):
-    wl = W.make_config(cfg)
-    rows = "all"
-    if cfg in (2, 3):                             # big batches: the oracle checks a sample
-        rng = np.random.default_rng(cfg)
-        rows = sorted(rng.choice(wl.num_q_tokens, size=min(96, wl.num_q_tokens), replace=False).tolist())
-    check_fused_equals_separate(wl, f"config{cfg}", oracle_rows=rows)
+    check_fused_equals_separate(W.make_config(cfg), f"config{cfg}")
 
 
 FUSED_EDGE = [
