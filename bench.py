@@ -1,34 +1,37 @@
 """Benchmark of the paged attention path on one MI355X.
 
 A step = the append of the batch's new tokens + attention over the batch (every
-row of the hot path), on seeded synthetic inputs already resident in HBM: by
-default one paged_attention_append call (the append fused into the attention
-call), with --step separate kv_append then paged_attention (the 8-bit cache
-always uses its two calls).  Default workload: the Llama-3-8B-shaped decode layer (64
-sequences, contexts U{128..4096}, 32 query / 8 KV heads, d 128, 16-token
-blocks).  Several device copies of the batch are cycled so consecutive steps
-do not re-read the same lines from the 256 MB last-level cache.
+row of the hot path), on seeded synthetic inputs already resident in HBM: one
+paged_attention_append call (the append fused into the attention call; with
+--step separate, kv_append then paged_attention; the 8-bit cache always uses
+its two calls).  Default workload (the headline): the 70B-class decode layer
+at full single-GPU shape (256 sequences, contexts lognormal with median 1024
+capped at 8192, 64 query / 8 KV heads, d 128, 16-token blocks).  Several
+device copies of the batch are cycled so consecutive steps do not re-read the
+same lines from the 256 MB last-level cache.
 
 Prints ONE JSON line on stdout:
   value         KV-read GB/s of the whole step: algorithmic K+V bytes (every
-                cached token of every sequence read once) / step time;
-  roofline      the attention call (fused append + split-K decode + merge),
-                timed with HIP events on its stream around every call of the
-                timed region, against the 8 TB/s HBM peak; `traffic` comes from rocprofv3
-                FETCH_SIZE/WRITE_SIZE counters stored under profiles/ (null if
-                the kernels changed since);
-  call_us       median / p10 / p90 of those per-call times, and the median
-                with the same copy re-read (hot last-level cache);
-  prefill       the other half of the metric: the chunked-prefill rows of the
-                mixed batch (8 chunks of 512 rows over prefixes of 0..2048
-                tokens, 32/8 heads, d 128) in a call of their own, TFLOP/s of
-                causal pairs against the 2.5 PFLOP/s bf16 peak;
-  separate_calls the same steps through kv_append + paged_attention;
-  mixed         (mixed batch only) decode-only and prefill-only sub-batch times;
-  append        kv_append alone at T = 64, 4288 and 65536 tokens (HBM GB/s);
-  measured_peaks a device copy and a bf16 GEMM through torch, and the library's
-                streaming-read and matrix-core-loop probes, for context;
-  cpu_baseline  the float64 CPU oracle on a bounded sample of the same batch.
+                cached token of every sequence read once) / wall-clock step time;
+  roofline      the attention call (fused append + split-K decode + merge, and
+                prefill on the mixed batch), timed with one HIP event pair
+                around the timed region on its stream, against the 8 TB/s HBM
+                peak; `traffic` comes from rocprofv3 FETCH_SIZE/WRITE_SIZE
+                counters stored under profiles/ (null if the kernels changed since);
+  cpu_baseline  the float64 CPU oracle on a bounded sample of the same batch,
+                scaled to the whole batch (same unit as value), with the
+                GPU/oracle time ratio;
+  per_config    the same record for the other configurations: the tiny batch
+                (GPU call time; oracle single-threaded and on all cores), the
+                Llama-3-8B decode layer, the mixed batch with its shared prefix
+                (mixed call, decode-only and prefill-only sub-batches: decode on
+                unique and logical bytes, prefill in TFLOP/s of causal pairs
+                against the 2.5 PFLOP/s bf16 peak) and the long-context batch;
+                each with its roofline, 8-bit-pool call and CPU baseline;
+  call_us, separate_calls, graph, append, allocator, measured_peaks:
+                single-call spread, the two-call step, a HIP-graph replay,
+                kv_append alone at T = 64, 4288, 65536, the host allocator, and
+                a device copy / GEMM / the library's read and matrix-core probes.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config i]
 """
@@ -88,43 +91,59 @@ def pct(xs, q):
     return float(np.percentile(np.asarray(xs, dtype=np.float64), q))
 
 
-def cpu_baseline(wl, k2, v2, budget_s: float, f8=None):
-    """Time the float64 oracle (as it stands) on whole sequences of the batch until the budget is used
-    (with ``f8``: the 8-bit pools' oracle; bytes then count one per value)."""
+def cpu_baseline(wl, k2, v2, budget_s: float, f8=None, gpu_call_s=None, threads=None):
+    """Time the float64 oracle (as it stands) on whole sequences of the batch, in a seeded random
+    order, until ``budget_s`` seconds are used (at least one sequence), and scale to the whole
+    batch by the oracle's work per sequence (query rows x keys).  ``value`` is in the unit of the
+    GPU figure: K+V bytes of the whole batch (one per value with ``f8``: the 8-bit pools'
+    oracle) / the estimated whole-batch oracle time.  ``threads``: BLAS thread limit (None =
+    all).  With ``gpu_call_s`` the record carries the whole-batch time ratio oracle / GPU."""
+    import numpy as np
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+    from threadpoolctl import threadpool_info, threadpool_limits
     cores = len(os.sched_getaffinity(0))
-    bytes_done, t_used, seqs, passes = 0, 0.0, 0, 0
     qsl = wl.query_start_loc
-    t0 = time.perf_counter()
-    # whole sequences, in batch order, repeating the batch until ~budget seconds of oracle work
-    while t_used < budget_s:
-        for s in range(wl.num_seqs):
-            rows = list(range(int(qsl[s]), int(qsl[s + 1])))
-            if not rows:
-                continue
-            if f8 is None:
-                oracle.paged_attention(wl.q, k2, v2, wl.block_tables, wl.seq_lens, wl.query_start_loc,
-                                       wl.num_kv_heads, wl.scale, rows=rows)
-            else:
-                oracle.paged_attention_fp8(wl.q, k2, v2, wl.block_tables, wl.seq_lens, wl.query_start_loc,
-                                           wl.num_kv_heads, wl.scale, f8.k_scale, f8.v_scale, rows=rows)
-            seqs += 1
-            bytes_done += wl.kv_read_bytes([s]) // (1 if f8 is None else 2)
-            t_used = time.perf_counter() - t0
-            if t_used >= budget_s:
-                break
-        passes += 1
-    return {"value": round(bytes_done / t_used / 1e9, 4), "unit": "GB/s", "cores": int(min(threads, cores)),
-            "kind": "oracle",
-            "sample": f"{seqs} sequence passes over the {wl.num_seqs}-sequence batch (whole sequences, all heads, "
-                      f"batch repeated {passes}x), "
-                      f"{bytes_done / 1e6:.1f} MB of K/V in {t_used:.1f} s; float64 NumPy oracle; "
-                      f"BLAS threads {threads}, host cores {cores}"}
+    ql = np.diff(qsl).astype(np.int64)
+    L = wl.seq_lens.astype(np.int64)
+    seqs = [s for s in range(wl.num_seqs) if ql[s] > 0]
+    work = {s: int(ql[s]) * int(L[s]) for s in seqs}
+    total_work = sum(work.values())
+    order = np.random.default_rng(12345).permutation(len(seqs))
+    done_work, n_done, passes = 0, 0, 0
+    ctx = threadpool_limits(limits=threads) if threads else threadpool_limits(limits=None)
+    with ctx:
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        t0 = time.perf_counter()
+        elapsed = 0.0
+        while elapsed < budget_s or n_done == 0:
+            for idx in order:
+                s = seqs[int(idx)]
+                rows = list(range(int(qsl[s]), int(qsl[s + 1])))
+                if f8 is None:
+                    oracle.paged_attention(wl.q, k2, v2, wl.block_tables, wl.seq_lens, wl.query_start_loc,
+                                           wl.num_kv_heads, wl.scale, rows=rows)
+                else:
+                    oracle.paged_attention_fp8(wl.q, k2, v2, wl.block_tables, wl.seq_lens, wl.query_start_loc,
+                                               wl.num_kv_heads, wl.scale, f8.k_scale, f8.v_scale, rows=rows)
+                done_work += work[s]
+                n_done += 1
+                elapsed = time.perf_counter() - t0
+                if elapsed >= budget_s:
+                    break
+            passes += 1
+    est_batch_s = elapsed * total_work / done_work
+    batch_bytes = wl.kv_read_bytes() // (1 if f8 is None else 2)
+    rec = {"value": round(batch_bytes / est_batch_s / 1e9, 4), "unit": "GB/s",
+           "cores": int(min(blas_threads, cores)), "kind": "oracle",
+           "sample": f"{n_done} whole sequences of the {wl.num_seqs}-sequence batch in a seeded random order "
+                     f"({done_work / total_work:.3f} of the batch's rows x keys) in {elapsed:.1f} s, scaled to the "
+                     f"whole batch: {est_batch_s:.2f} s; float64 NumPy oracle"
+                     + (" over the 8-bit pools" if f8 is not None else "")
+                     + f"; BLAS threads {blas_threads}, host cores {cores}",
+           "est_batch_s": round(est_batch_s, 4)}
+    if gpu_call_s:
+        rec["oracle_over_gpu_time"] = round(est_batch_s / gpu_call_s, 1)
+    return rec
 
 
 class Device:
@@ -276,7 +295,7 @@ def graph_report(pkv, c, wl, torch, n=30):
             "graph_step_us_p10": round(pct(ms, 10) * 1e3, 3), "replays": n}
 
 
-def fp8_report(pkv, d, torch, stream, bf16_call_us, n=30, copies=3):
+def fp8_report(pkv, d, torch, stream, bf16_call_us, n=100, copies=3):
     """The same batch over 8-bit (E4M3) pools: kv_append_fp8 of the step's tokens, then
     paged_attention_fp8 timed like the bf16 call (copies cycled); GB/s of the code bytes."""
     import workloads
@@ -417,22 +436,221 @@ def measured_peaks(torch, dev, stream):
             "mfma_bf16_note": "pkv_peak_mfma_bf16: back-to-back 32x32x16 bf16 MFMAs, 2 waves per SIMD, no memory"}
 
 
+def time_step(pkv, torch, stream, wl, copies, mode, steps, warmup, f8=None):
+    """Time `steps` steps of the batch after `warmup` untimed ones, cycling the device copies.
+
+    mode "fused": one paged_attention_append call per step; "separate": kv_append then
+    paged_attention; "fp8": kv_append_fp8 then paged_attention_fp8.  Every call is checked
+    and marshalled once per copy (PreparedCall), so the timed loop issues bare C calls and the
+    host stays ahead of the device.  Returns the wall-clock step time, the attention call time
+    (one HIP event pair around the timed region on the library's stream, / steps: with the
+    fused step the region holds nothing but those calls; no event inside the region, since
+    each one costs the stream ~5 us of idle time), and single-call times of a later pass."""
+    for c in copies:
+        t = c.t
+        if mode == "fp8":
+            c.append = pkv.kv_append_fp8(t["k_new"], t["v_new"], t["slots"], t["kc"], t["vc"], f8.k_scale,
+                                         f8.v_scale, stream=stream, prepare=True)
+            c.attend = pkv.paged_attention_fp8(t["out"], t["q"], t["kc"], t["vc"], t["bt"], t["sl"], t["qsl"],
+                                               wl.scale, wl.max_query_len, f8.k_scale, f8.v_scale,
+                                               workspace=t["ws"], stream=stream, prepare=True)
+            c.fused = None
+        else:
+            c.append = pkv.kv_append(t["k_new"], t["v_new"], t["slots"], t["kc"], t["vc"], stream=stream,
+                                     prepare=True)
+            c.attend = pkv.paged_attention(t["out"], t["q"], t["kc"], t["vc"], t["bt"], t["sl"], t["qsl"],
+                                           wl.scale, wl.max_query_len, workspace=t["ws"], stream=stream,
+                                           prepare=True)
+            c.fused = pkv.paged_attention_append(t["out"], t["q"], t["k_new"], t["v_new"], t["slots"], t["kc"],
+                                                 t["vc"], t["bt"], t["sl"], t["qsl"], wl.scale, wl.max_query_len,
+                                                 workspace=t["ws"], stream=stream, prepare=True)
+    fused = mode == "fused"
+
+    def run(n, evs=None):
+        for i in range(n):
+            c = copies[i % len(copies)]
+            if fused:
+                if evs is not None:
+                    evs[i][0].record(stream)
+                c.fused()
+            else:
+                c.append()
+                if evs is not None:
+                    evs[i][0].record(stream)
+                c.attend()
+            if evs is not None:
+                evs[i][1].record(stream)
+
+    run(warmup)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    run(steps)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    call_ms = ev0.elapsed_time(ev1) / steps
+    n_spread = min(steps, 30)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_spread)]
+    run(n_spread, evs)
+    torch.cuda.synchronize()
+    spread = [a.elapsed_time(b) for a, b in evs]
+    hot = time_calls(lambda: (copies[0].fused if fused else copies[0].attend)(), 10, 2, stream, torch)
+    return {"ms_per_step": elapsed * 1e3 / steps, "call_ms": call_ms, "spread_ms": spread, "hot_ms": hot}
+
+
+def device_copies(wl, dev, torch, pkv, n_copies, f8=None):
+    """n_copies device copies of the batch (bf16 pools, or the 8-bit pools of ``f8``), each with
+    its own output and workspace."""
+    base = Device(wl, dev, torch)
+    if f8 is not None:
+        base.t["kc"] = torch.from_numpy(f8.k_cache).to(dev)
+        base.t["vc"] = torch.from_numpy(f8.v_cache).to(dev)
+    copies = [base] + [base.clone() for _ in range(n_copies - 1)]
+    ws_bytes = pkv.workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
+                                   wl.max_blocks_per_seq, wl.block_size, wl.max_query_len)
+    for c in copies:
+        c.t["out"] = torch.empty_like(c.t["q"])
+        c.t["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    return copies
+
+
+def step_record(wl, cfg, st, mode, kv_bytes, uniq_bytes, traffic_key):
+    """The step's throughput and the attention call's roofline (HBM) from a time_step result."""
+    pre = wl.prefill_seqs()
+    dec = wl.decode_seqs()
+    achieved = uniq_bytes / (st["call_ms"] * 1e-3) / 1e9
+    kernel = {"fused": "paged_attention_append call (append + ",
+              "separate": "kv_append + paged_attention step (",
+              "fp8": "kv_append_fp8 + paged_attention_fp8 step ("}[mode]
+    kernel += "split-K decode + LSE merge" + (" + prefill" if len(pre) else "") + ")"
+    return {
+        "ms_per_step": round(st["ms_per_step"], 5),
+        "step_GBps": round(kv_bytes / (st["ms_per_step"] * 1e-3) / 1e9, 2),
+        "decode_tokens_per_s": round(len(dec) / (st["ms_per_step"] * 1e-3), 1),
+        "roofline": {"bound": "hbm", "kernel": kernel,
+                     "timing": "HIP events around the timed region on the library's stream, / steps",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "avg_call_us": round(st["call_ms"] * 1e3, 3),
+                     "algorithmic_bytes_per_call": uniq_bytes,
+                     "algorithmic_bytes_note": "K+V bytes of every cached token of every sequence, each physical "
+                                               "block of a shared prefix counted once"
+                                               + ("; one byte per value (E4M3 codes)" if mode == "fp8" else ""),
+                     "traffic": traffic_from_profile(cfg, traffic_key)},
+        "call_us": {"median": round(pct(st["spread_ms"], 50) * 1e3, 3),
+                    "p10": round(pct(st["spread_ms"], 10) * 1e3, 3),
+                    "p90": round(pct(st["spread_ms"], 90) * 1e3, 3),
+                    "hot_cache_median": round(pct(st["hot_ms"], 50) * 1e3, 3),
+                    "note": "event pair around each " + ("call" if mode == "fused" else "attention call")
+                            + " in a pass after the timed region"},
+    }
+
+
+def config_record(cfg, args, torch, pkv, dev, stream, headline=False):
+    """Everything measured on one configuration: the timed step with its roofline, the mixed
+    batch's sub-batches, the 8-bit pools' call, the two-call step and a graph replay (headline
+    only), and the CPU oracle baseline."""
+    import numpy as np
+    import oracle
+    import workloads
+    log(f"config {cfg}: generating ...")
+    wl = workloads.make_config(cfg)
+    fp8 = headline and args.kv == "fp8"
+    f8 = workloads.fp8_pools(wl) if fp8 else None
+    mode = "fp8" if fp8 else args.step
+    copies = device_copies(wl, dev, torch, pkv, args.copies, f8)
+    base = copies[0]
+    st = time_step(pkv, torch, stream, wl, copies, mode, args.steps, args.warmup, f8)
+    div = 2 if fp8 else 1                        # one byte per value for E4M3 pools
+    kv_bytes, uniq_bytes = wl.kv_read_bytes() // div, wl.unique_kv_read_bytes() // div
+    dec, pre = wl.decode_seqs(), wl.prefill_seqs()
+    rec = {"workload": workload_desc(wl), "config_index": cfg, "seed": wl.meta["seed"],
+           "kv_bytes_per_step": kv_bytes, "unique_kv_bytes_per_step": uniq_bytes,
+           "decode_rows": int(len(dec)), "prefill_rows": int(wl.query_lens[pre].sum()) if len(pre) else 0,
+           "appended_tokens": wl.num_q_tokens, "device_copies_cycled": len(copies),
+           "kv_cache": "e4m3, per-pool scales 2^-4 (K), 2^-3 (V)" if fp8 else "bf16",
+           "steps": args.steps, "warmup": args.warmup,
+           "step": {"fused": "paged_attention_append (kv_append fused into the attention call)",
+                    "separate": "kv_append + paged_attention", "fp8": "kv_append_fp8 + paged_attention_fp8"}[mode]}
+    rec.update(step_record(wl, cfg, st, mode, kv_bytes, uniq_bytes,
+                           {"fused": "paged_attention_append", "separate": "paged_attention",
+                            "fp8": "paged_attention_fp8"}[mode]))
+    log(f"config {cfg}: step {st['ms_per_step'] * 1e3:.1f} us, call {st['call_ms'] * 1e3:.1f} us, "
+        f"{rec['roofline']['frac']:.3f} of HBM peak")
+    if cfg == 0:
+        rec["roofline"]["note"] = "a few KiB of K/V: launch-bound, the fraction is not meaningful"
+    if len(pre) and not fp8 and cfg != 0:
+        # the mixed batch: decode-only and prefill-only sub-batches in calls of their own
+        dms, dmed = sub_attention_ms(pkv, base, base.subset(dec), wl.scale, stream, torch)
+        ub, lb = wl.unique_kv_read_bytes(dec), wl.kv_read_bytes(dec)
+        rec["decode_only"] = {"call_us_avg": round(dmed * 1e3, 3), "call_us_median": round(pct(dms, 50) * 1e3, 3),
+                              "unique_bytes": ub, "logical_bytes": lb,
+                              "roofline": {"bound": "hbm", "achieved": round(ub / (dmed * 1e-3) / 1e9, 1),
+                                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                           "frac": round(ub / (dmed * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                           "note": "unique bytes (shared prefix blocks once)"},
+                              "logical_GBps": round(lb / (dmed * 1e-3) / 1e9, 1)}
+        rec["prefill_only"] = prefill_report(pkv, base, stream, torch)
+        flops = rec["prefill_only"]["flops_per_call"]
+        floor_s = max(uniq_bytes / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12))
+        sum_s = uniq_bytes / (HBM_PEAK_GBS * 1e9) + flops / (BF16_PEAK_TFLOPS * 1e12)
+        rec["roofline"]["mixed_floor_us"] = round(floor_s * 1e6, 2)
+        rec["roofline"]["mixed_frac"] = round(floor_s / (st["call_ms"] * 1e-3), 4)
+        rec["roofline"]["mixed_sum_floor_us"] = round(sum_s * 1e6, 2)
+        rec["roofline"]["mixed_note"] = ("floor = max(unique bytes / 8 TB/s, causal-pair flops / 2.5 PFLOP/s); "
+                                         "sum floor = the two added")
+    if headline and mode == "fused" and not args.no_extras:
+        sep = time_step(pkv, torch, stream, wl, copies, "separate", args.steps, 3)
+        rec["separate_calls"] = {"step_us": round(sep["ms_per_step"] * 1e3, 3),
+                                 "step_GBps": round(kv_bytes / (sep["ms_per_step"] * 1e-3) / 1e9, 2),
+                                 "attention_call_us_median": round(pct(sep["spread_ms"], 50) * 1e3, 3)}
+        rec["graph"] = graph_report(pkv, base, wl, torch)
+    if not fp8 and not args.no_extras:
+        log(f"config {cfg}: 8-bit pools ...")
+        rec["fp8"] = fp8_report(pkv, base, torch, stream, rec["roofline"]["avg_call_us"])
+        if len(pre) and cfg != 0:
+            rec["prefill_only"]["fp8"] = prefill_fp8_report(pkv, base, torch, stream)
+    del copies, base
+    torch.cuda.empty_cache()
+    if not args.no_cpu:
+        log(f"config {cfg}: CPU oracle ...")
+        gpu_s = st["call_ms"] * 1e-3
+        if fp8:
+            k2, v2 = oracle.kv_append_fp8(f8.k_cache, f8.v_cache, wl.k_new, wl.v_new, wl.slot_mapping,
+                                          f8.k_scale, f8.v_scale)
+        else:
+            k2, v2 = oracle.kv_append(wl.k_cache, wl.v_cache, wl.k_new, wl.v_new, wl.slot_mapping)
+        budget = args.cpu_budget if headline else args.cpu_budget_other
+        rec["cpu_baseline"] = cpu_baseline(wl, k2, v2, budget, f8, gpu_call_s=gpu_s)
+        if cfg == 0:
+            rec["cpu_baseline_single_thread"] = cpu_baseline(wl, k2, v2, min(budget, 2.0), f8, gpu_call_s=gpu_s,
+                                                             threads=1)
+        del k2, v2
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", type=int, default=1, help="workload: 0..4 (1 = Llama-3-8B decode)")
+    ap.add_argument("--config", type=int, default=2, help="headline workload: 0..4 (2 = 70B-class decode)")
     ap.add_argument("--copies", type=int, default=3, help="device copies of the batch cycled per step")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle time for the headline configuration's cpu_baseline")
+    ap.add_argument("--cpu-budget-other", type=float, default=6.0,
+                    help="seconds of oracle time for each other configuration's cpu_baseline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--kv", choices=["bf16", "fp8"], default="bf16",
-                    help="cache element type of the timed step: bf16 (default) or 8-bit E4M3 codes with "
+                    help="cache element type of the headline step: bf16 (default) or 8-bit E4M3 codes with "
                          "per-pool scales (kv_append_fp8 + paged_attention_fp8; implies --no-extras)")
     ap.add_argument("--step", choices=["fused", "separate"], default="fused",
                     help="timed step: paged_attention_append, or kv_append then paged_attention (bf16 cache)")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the prefill, append and peak measurements (step timing and roofline only)")
+                    help="the headline configuration only (no other configurations, sub-batches, 8-bit "
+                         "pools, append sweep, allocator or peak measurements)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the step, run a plain device copy of MIB MiB --steps times "
                          "(reference kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -444,9 +662,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
-    import workloads
     import paged_kv_cache_tables_amd as pkv
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
@@ -463,221 +679,58 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
                           "steps": args.steps}), flush=True)
         return
-
-    log(f"generating config {args.config} ...")
-    wl = workloads.make_config(args.config)
-    base = Device(wl, dev, torch)
-    fp8 = args.kv == "fp8"
-    if fp8:
+    if args.kv == "fp8":
         args.no_extras = True
-        f8 = workloads.fp8_pools(wl)
-        wl.drop_pools()
-        base.t["kc"] = torch.from_numpy(f8.k_cache).to(dev)
-        base.t["vc"] = torch.from_numpy(f8.v_cache).to(dev)
-    copies = [base] + [base.clone() for _ in range(args.copies - 1)]
-    ws_bytes = pkv.workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
-                                   wl.max_blocks_per_seq, wl.block_size, wl.max_query_len)
-    for c in copies:
-        c.t["out"] = torch.empty_like(c.t["q"])
-        c.t["ws"] = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    # Each call is checked and marshalled once per device copy (PreparedCall), so the timed
-    # loop issues bare C calls: the host cost per step stays below the device time.
-    def prep_append(c):
-        t = c.t
-        if fp8:
-            return pkv.kv_append_fp8(t["k_new"], t["v_new"], t["slots"], t["kc"], t["vc"], f8.k_scale, f8.v_scale,
-                                     stream=stream, prepare=True)
-        return pkv.kv_append(t["k_new"], t["v_new"], t["slots"], t["kc"], t["vc"], stream=stream, prepare=True)
-
-    def prep_fused(c):
-        t = c.t
-        return pkv.paged_attention_append(t["out"], t["q"], t["k_new"], t["v_new"], t["slots"], t["kc"], t["vc"],
-                                          t["bt"], t["sl"], t["qsl"], wl.scale, wl.max_query_len, workspace=t["ws"],
-                                          stream=stream, prepare=True)
-
-    def prep_attend(c):
-        t = c.t
-        if fp8:
-            return pkv.paged_attention_fp8(t["out"], t["q"], t["kc"], t["vc"], t["bt"], t["sl"], t["qsl"], wl.scale,
-                                           wl.max_query_len, f8.k_scale, f8.v_scale, workspace=t["ws"],
-                                           stream=stream, prepare=True)
-        return pkv.paged_attention(t["out"], t["q"], t["kc"], t["vc"], t["bt"], t["sl"], t["qsl"], wl.scale,
-                                   wl.max_query_len, workspace=t["ws"], stream=stream, prepare=True)
-
-    for c in copies:
-        c.append, c.attend = prep_append(c), prep_attend(c)
-        c.fused = None if fp8 else prep_fused(c)
-
-    def append(c):
-        c.append()
-
-    def fused_step(c):
-        c.fused()
-
-    def attend(c):
-        c.attend()
-
-    use_fused = args.step == "fused" and not fp8   # the 8-bit cache has no fused call
-
-    def run_steps(n, fused_call, evs=None):
-        for i in range(n):
-            c = copies[i % len(copies)]
-            if fused_call:
-                if evs is not None:
-                    evs[i][0].record(stream)
-                fused_step(c)
-            else:
-                append(c)
-                if evs is not None:
-                    evs[i][0].record(stream)
-                attend(c)
-            if evs is not None:
-                evs[i][1].record(stream)
-
-    run_steps(args.warmup, use_fused)
-    torch.cuda.synchronize()
-
-    # Timed region: K steps back to back, one HIP event pair around the region on the
-    # library's stream (an event recorded between calls costs the stream ~5 us of idle
-    # time, so none is recorded inside the region).  With the fused step the region holds
-    # nothing but the K attention calls, so its event time / K is the call's duration.
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    run_steps(args.steps, use_fused)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    region_ms = ev0.elapsed_time(ev1)
-
-    ms_per_step = elapsed * 1e3 / args.steps
-    attn_avg_ms = region_ms / args.steps
-    # spread of single calls: a second pass with an event pair around each call
-    n_spread = min(args.steps, 30)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_spread)]
-    run_steps(n_spread, use_fused, evs)
-    torch.cuda.synchronize()
-    attn_ms = [a.elapsed_time(b) for a, b in evs]
-    kv_bytes = wl.kv_read_bytes() // (2 if fp8 else 1)          # one byte per value for E4M3 pools
-    uniq_bytes = wl.unique_kv_read_bytes() // (2 if fp8 else 1)
-    dec = wl.decode_seqs()
-    pre = wl.prefill_seqs()
-    value = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = uniq_bytes / (attn_avg_ms * 1e-3) / 1e9
-    hot_ms = time_calls(lambda: (fused_step if use_fused else attend)(copies[0]), 10, 2, stream, torch)
-
+    head = config_record(args.config, args, torch, pkv, dev, stream, headline=True)
+    fp8 = args.kv == "fp8"
     result = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": head["step_GBps"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16 (E4M3 K/V cache)" if fp8 else "bf16",
         "data": "synthetic",
-        "config": {"workload": workload_desc(wl), "config_index": args.config, "seed": wl.meta["seed"],
-                   "kv_bytes_per_step": kv_bytes, "unique_kv_bytes_per_step": uniq_bytes,
-                   "decode_rows": int(len(dec)), "prefill_rows": int(wl.query_lens[pre].sum()) if len(pre) else 0,
-                   "appended_tokens": wl.num_q_tokens, "device_copies_cycled": len(copies),
-                   "kv_cache": "e4m3, per-pool scales 2^-4 (K), 2^-3 (V)" if fp8 else "bf16"},
-        "decode_tokens_per_s": round(len(dec) / (ms_per_step * 1e-3), 1),
-        "step": ("paged_attention_append (kv_append fused into the attention call)" if use_fused
-                 else "kv_append_fp8 + paged_attention_fp8" if fp8 else "kv_append + paged_attention"),
-        "roofline": {"bound": "hbm", "kernel": ("paged_attention_append call (append + " if use_fused else
-                                                "kv_append_fp8 + paged_attention_fp8 step (" if fp8 else
-                                                "kv_append + paged_attention step (")
-                     + "split-K decode + LSE merge" + (" + prefill" if len(pre) else "") + ")",
-                     "timing": "HIP events around the timed region on the library's stream, / steps",
-                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "avg_call_us": round(attn_avg_ms * 1e3, 3),
-                     "algorithmic_bytes_per_call": uniq_bytes,
-                     "traffic": traffic_from_profile(args.config, "paged_attention_append" if use_fused else
-                                                     "paged_attention_fp8" if fp8 else "paged_attention")},
-        "call_us": {"median": round(pct(attn_ms, 50) * 1e3, 3), "p10": round(pct(attn_ms, 10) * 1e3, 3),
-                    "p90": round(pct(attn_ms, 90) * 1e3, 3),
-                    "hot_cache_median": round(pct(hot_ms, 50) * 1e3, 3),
-                    "note": "event pair around each " + ("call" if use_fused else "attention call")
-                            + " in a pass after the timed region"},
+        "config": {k: head[k] for k in ("workload", "config_index", "seed", "kv_bytes_per_step",
+                                        "unique_kv_bytes_per_step", "decode_rows", "prefill_rows",
+                                        "appended_tokens", "device_copies_cycled", "kv_cache")},
+        "decode_tokens_per_s": head["decode_tokens_per_s"],
+        "step": head["step"],
+        "roofline": head["roofline"],
+        "cpu_baseline": head.get("cpu_baseline"),
+        "call_us": head["call_us"],
     }
-    log(f"step {ms_per_step * 1e3:.1f} us, attention call {attn_avg_ms * 1e3:.1f} us, "
-        f"{value:.0f} GB/s step, {achieved:.0f} GB/s attention")
-
-    if use_fused and not args.no_extras:
-        # the same batch through the two separate calls, for comparison
-        nsep = args.steps
-        run_steps(3, False)
-        torch.cuda.synchronize()
-        ts0 = time.perf_counter()
-        run_steps(nsep, False)
-        torch.cuda.synchronize()
-        sep_step = (time.perf_counter() - ts0) / nsep
-        sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(30)]
-        run_steps(30, False, sev)
-        torch.cuda.synchronize()
-        sep_ms = [a.elapsed_time(b) for a, b in sev]
-        result["separate_calls"] = {"step_us": round(sep_step * 1e6, 3),
-                                    "step_GBps": round(kv_bytes / sep_step / 1e9, 2),
-                                    "attention_call_us_median": round(pct(sep_ms, 50) * 1e3, 3),
-                                    "attention_call_GBps": round(uniq_bytes / (pct(sep_ms, 50) * 1e-3) / 1e9, 2)}
+    for k in ("separate_calls", "graph", "fp8", "decode_only", "prefill_only"):
+        if k in head:
+            result[k] = head[k]
     if not args.no_extras:
-        result["graph"] = graph_report(pkv, copies[0], wl, torch)
-        log("8-bit pools ...")
-        result["fp8"] = fp8_report(pkv, base, torch, stream, result["roofline"]["avg_call_us"])
-        if len(pre):
-            # the mixed batch itself: decode-only and prefill-only sub-batches
-            dms, dmed = sub_attention_ms(pkv, base, base.subset(dec), wl.scale, stream, torch)
-            ub = wl.unique_kv_read_bytes(dec)
-            result["mixed"] = {"decode_only_call_us_avg": round(dmed * 1e3, 3),
-                               "decode_only_unique_GBps": round(ub / (dmed * 1e-3) / 1e9, 1),
-                               "decode_only_logical_GBps": round(wl.kv_read_bytes(dec) / (dmed * 1e-3) / 1e9, 1),
-                               "mixed_call_us_avg": result["roofline"]["avg_call_us"]}
-            result["prefill"] = prefill_report(pkv, base, stream, torch)
-            result["prefill"]["fp8"] = prefill_fp8_report(pkv, base, torch, stream)
-            result["mixed"]["prefill_only_call_us_avg"] = result["prefill"]["call_us_avg"]
-            del copies
-        else:
-            del copies, base
-            torch.cuda.empty_cache()
-            log("generating the mixed batch for its prefill rows ...")
-            wl3 = workloads.make_config(3)
-            d3 = Device(wl3, dev, torch)
-            # the pools must hold this step's tokens before attention reads them
-            pkv.kv_append(d3.t["k_new"], d3.t["v_new"], d3.t["slots"], d3.t["kc"], d3.t["vc"], stream=stream)
-            result["prefill"] = prefill_report(pkv, d3, stream, torch)
-            result["prefill"]["fp8"] = prefill_fp8_report(pkv, d3, torch, stream)
-            del d3
-        torch.cuda.empty_cache()
+        result["per_config"] = {}
+        for cfg in (0, 1, 2, 3, 4):
+            if cfg != args.config:
+                result["per_config"][f"config{cfg}"] = config_record(cfg, args, torch, pkv, dev, stream)
+        log("append, allocator, peaks ...")
         result["append"] = append_report(pkv, dev, torch, stream)
         result["allocator"] = allocator_report(pkv)
         result["measured_peaks"] = measured_peaks(torch, dev, stream)
+        achieved = result["roofline"]["achieved"]
         result["measured_peaks"]["decode_frac_of_device_copy"] = round(
             achieved / result["measured_peaks"]["device_copy_GBps"], 4)
         result["measured_peaks"]["decode_frac_of_stream_read"] = round(
             achieved / result["measured_peaks"]["stream_read_GBps"], 4)
-        if "prefill" in result:
+        c3 = result["per_config"].get("config3") or (head if args.config == 3 else None)
+        if c3 is not None and "prefill_only" in c3:
+            tf = c3["prefill_only"]["roofline"]["achieved"]
             result["measured_peaks"]["prefill_frac_of_bf16_gemm"] = round(
-                result["prefill"]["roofline"]["achieved"] / result["measured_peaks"]["bf16_gemm_TFLOPs"], 4)
+                tf / result["measured_peaks"]["bf16_gemm_TFLOPs"], 4)
             result["measured_peaks"]["prefill_frac_of_mfma_loop"] = round(
-                result["prefill"]["roofline"]["achieved"] / result["measured_peaks"]["mfma_bf16_TFLOPs"], 4)
-
-    if not args.no_cpu:
-        import oracle
-        if fp8:
-            k2, v2 = oracle.kv_append_fp8(f8.k_cache, f8.v_cache, wl.k_new, wl.v_new, wl.slot_mapping,
-                                          f8.k_scale, f8.v_scale)
-            result["cpu_baseline"] = cpu_baseline(wl, k2, v2, args.cpu_budget, f8)
-        else:
-            k2, v2 = oracle.kv_append(wl.k_cache, wl.v_cache, wl.k_new, wl.v_new, wl.slot_mapping)
-            result["cpu_baseline"] = cpu_baseline(wl, k2, v2, args.cpu_budget)
-    else:
-        result["cpu_baseline"] = None
+                tf / result["measured_peaks"]["mfma_bf16_TFLOPs"], 4)
     print(json.dumps(result), flush=True)
 
 

@@ -460,13 +460,14 @@ class Fp8Pools:
     v_scale: float
 
 
-def _fp8_code_draws(rng: np.random.Generator, n: int, center: int) -> np.ndarray:
+def _fp8_code_draws(rng_of_chunk, n: int, center: int) -> np.ndarray:
     """n random E4M3 codes: random sign and mantissa, exponent field spread below
     ``center`` (a rounded normal with mean center - 1 and sd 1, clipped to
     1..center + 1, so magnitudes stay under 4 times 2^(center - 7) the way N(0,1)
     draws stay under a few units), about 1% with exponent field 0 (zeros and
     subnormals); never the NaN pattern.  Pure bit drawing: nothing is converted to or
-    from a number."""
+    from a number.  Chunks of 2^22 codes are drawn in parallel, chunk i from the
+    generator ``rng_of_chunk(i)``."""
     grid = np.arange(256) + 0.5
     top = min(15, center + 1)
     # exponent field of each 8-bit draw: inverse of a normal CDF sampled on 256 cells
@@ -476,15 +477,19 @@ def _fp8_code_draws(rng: np.random.Generator, n: int, center: int) -> np.ndarray
     e_of = np.minimum(e_of, top).astype(np.uint8)
     out = np.empty(n, dtype=np.uint8)
     step = 1 << 22
-    for a in range(0, n, step):
+
+    def chunk(i):
+        a = i * step
         b = min(n, a + step)
-        r = rng.integers(0, 1 << 32, size=b - a, dtype=np.uint32)
+        r = rng_of_chunk(i).integers(0, 1 << 32, size=b - a, dtype=np.uint32)
         sign = ((r >> 7) & 1).astype(np.uint8)
         m = (r & 7).astype(np.uint8)
         e = e_of[(r >> 8) & 0xFF]
         e = np.where(((r >> 16) & 0xFF) < 3, np.uint8(0), e)
         m = np.where(e == 15, np.minimum(m, 6), m)            # keep clear of S.1111.111
         out[a:b] = (sign << 7) | (e << 3) | m
+
+    _par_map(chunk, range((n + step - 1) // step))
     return out
 
 
@@ -497,9 +502,9 @@ def fp8_pools(wl: Workload, k_scale: float = 2.0 ** -4, v_scale: float = 2.0 ** 
     pools = []
     for which, sc in ((0, k_scale), (1, v_scale)):
         center = 7 + int(round(-math.log2(sc)))
-        rng = _rng(seed, cfg, _S_FP8, which)
         pool = np.full(shape, poison, dtype=np.uint8)
-        rows = _fp8_code_draws(rng, wl.cached_slots.size * wl.num_kv_heads * wl.head_dim, center)
+        rows = _fp8_code_draws(lambda i, which=which: _rng(seed, cfg, _S_FP8, which, i),
+                               wl.cached_slots.size * wl.num_kv_heads * wl.head_dim, center)
         pool.reshape(-1, wl.num_kv_heads, wl.head_dim)[wl.cached_slots] = rows.reshape(
             -1, wl.num_kv_heads, wl.head_dim)
         pools.append(pool)
