@@ -70,6 +70,7 @@ extern "C" {
 #define PKV_EWORKSPACE   (-3) /* workspace too small (see paged_attention)         */
 #define PKV_EHIP         (-4) /* a HIP launch reported an error                    */
 #define PKV_ENOSPACE     (-5) /* allocator: not enough blocks even after eviction   */
+#define PKV_ESCRATCH     (-6) /* the shape needs more than the static scratch holds */
 
 /*
  * kv_bytes_per_token -- bytes of K plus V that one token occupies in the cache.
@@ -216,6 +217,39 @@ PKV_API int paged_attention_append(void* out, const void* q, const void* k_new, 
                                    int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
                                    int32_t block_size, float scale, void* workspace, size_t* workspace_bytes,
                                    void* stream);
+
+/*
+ * paged_attention_append_noalloc -- paged_attention_append without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Same arguments (minus workspace / workspace_bytes), same kernels and same
+ * result, pools and out bit for bit.  The split-K partials and the prefill
+ * work list go to a static device array of the library, PKV_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) per GPU, held by each GPU the library runs on until the process
+ * ends; its address is looked up once per device on the first call there.
+ * The call allocates, frees and clears nothing: the scratch needs no
+ * initialisation (every value is written before it is read within a call).
+ *
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap on
+ * one GPU (different streams without an ordering between them) race and give
+ * unspecified results.  Order them on one stream or with events.
+ *
+ * Returns what paged_attention_append returns, or PKV_ESCRATCH (nothing
+ * enqueued) when the shape needs more scratch than PKV_NOALLOC_SCRATCH_BYTES
+ * (paged_attention's workspace query gives the size a shape needs; e.g. 64
+ * sequences of up to 4096 tokens with 32 query heads of dimension 128 need
+ * about 10 MB, 4 sequences of 131072 tokens with 64 query heads about 34 MB).
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+PKV_API int paged_attention_append_noalloc(void* out, const void* q, const void* k_new, const void* v_new,
+                                           const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                                           const int32_t* block_tables, const int32_t* seq_lens,
+                                           const int32_t* query_start_loc, int32_t num_seqs,
+                                           int64_t num_q_tokens, int32_t max_blocks_per_seq,
+                                           int32_t max_query_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                           int32_t head_dim, int64_t num_blocks, int32_t block_size,
+                                           float scale, void* stream);
 
 /*
  * 8-bit (FP8 E4M3) cache.

@@ -11,6 +11,7 @@ if it is missing (build it with ``python -m paged_kv_cache_tables_amd.build``).
 """
 from ._lib import (  # noqa: F401
     META_FLAGS,
+    NOALLOC_SCRATCH_BYTES,
     AllocatorFull,
     BlockAllocator,
     PagedKVError,
@@ -24,6 +25,7 @@ from ._lib import (  # noqa: F401
     load_library,
     paged_attention,
     paged_attention_append,
+    paged_attention_append_noalloc,
     paged_attention_fp8,
     peak_mfma_bf16,
     peak_read,

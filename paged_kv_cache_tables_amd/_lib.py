@@ -15,7 +15,11 @@ _LIB_NAME = "libpagedkv.so"
 _lib = None
 
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape", -3: "workspace too small",
-          -4: "HIP launch error", -5: "no free blocks"}
+          -4: "HIP launch error", -5: "no free blocks",
+          -6: "shape needs more than the static scratch"}
+
+# bytes of the static device scratch behind paged_attention_append_noalloc (PKV_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class PagedKVError(RuntimeError):
@@ -55,6 +59,11 @@ def load_library() -> ctypes.CDLL:
                                            c_void_p, c_void_p, c_void_p, c_int32, c_int64, c_int32, c_int32,
                                            c_int32, c_int32, c_int32, c_int64, c_int32, c_float, c_void_p,
                                            c_size_p, c_void_p]
+    lib.paged_attention_append_noalloc.restype = c_int
+    lib.paged_attention_append_noalloc.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                                   c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int64,
+                                                   c_int32, c_int32, c_int32, c_int32, c_int32, c_int64, c_int32,
+                                                   c_float, c_void_p]
     lib.kv_append_fp8.restype = c_int
     lib.kv_append_fp8.argtypes = [c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_int64,
                                   c_int32, c_int32, c_int32, c_float, c_float, c_void_p]
@@ -318,6 +327,32 @@ def paged_attention_append(out, q, k_new, v_new, slot_mapping, k_cache, v_cache,
                    workspace.data_ptr(), ctypes.byref(have), _stream_ptr(stream, dev)],
                   prepare, (out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, seq_lens,
                             query_start_loc, workspace, have))
+
+
+def paged_attention_append_noalloc(out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables,
+                                   seq_lens, query_start_loc, scale: float, max_query_len: int, stream=None,
+                                   prepare=False):
+    """paged_attention_append with no workspace: the library's static per-GPU scratch
+    (NOALLOC_SCRATCH_BYTES) holds the partials, so neither the library nor this binding allocates
+    device memory.  Raises PagedKVError (status -6) for shapes that need more scratch than that.
+    Calls that may overlap on one GPU share the scratch and race: order them."""
+    import torch
+    NB, bs, Hkv, D, T, Hq, S, max_blocks, dev = _attention_shapes(
+        "paged_attention_append_noalloc", out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc,
+        torch.bfloat16)
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _check(t, n, torch.bfloat16, 3, dev)
+    _check(slot_mapping, "slot_mapping", torch.int64, 1, dev)
+    if k_new.shape != (T, Hkv, D) or v_new.shape != (T, Hkv, D) or slot_mapping.shape[0] != T:
+        raise ValueError("k_new/v_new/slot_mapping must have one row per query row")
+    lib = load_library()
+    return _issue("paged_attention_append_noalloc", lib.paged_attention_append_noalloc,
+                  [out.data_ptr(), q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(),
+                   k_cache.data_ptr(), v_cache.data_ptr(), block_tables.data_ptr(), seq_lens.data_ptr(),
+                   query_start_loc.data_ptr(), S, T, max_blocks, max_query_len, Hq, Hkv, D, NB, bs, float(scale),
+                   _stream_ptr(stream, dev)],
+                  prepare, (out, q, k_new, v_new, slot_mapping, k_cache, v_cache, block_tables, seq_lens,
+                            query_start_loc))
 
 
 def _check_codes(t, name, ndim, device):

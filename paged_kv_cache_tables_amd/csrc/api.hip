@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "kernels.h"
 #include "pagedkv.h"
@@ -75,6 +76,29 @@ WsLayout workspace_layout(int num_seqs, int Hq, int Hkv, int D, int max_blocks, 
   return w;
 }
 
+// Static scratch of paged_attention_append_noalloc: the workspace of one call, in a device
+// array of the library (each GPU the library runs on holds its own copy until the process
+// ends).  In host code the array's name is only a stand-in for the symbol, never a device
+// address: the address is looked up per device with hipGetSymbolAddress, with that device
+// current, on its first call, and only that pointer is handed to the kernels.
+constexpr size_t kNoallocScratchBytes = PKV_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+__device__ __attribute__((aligned(256))) char noalloc_scratch[kNoallocScratchBytes];
+
+void* noalloc_scratch_for_current_device() {
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch)) != hipSuccess || !p) return nullptr;
+    ptr[dev] = p;
+  }
+  return ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -99,6 +123,7 @@ const char* pkv_status_string(int status) {
     case PKV_EWORKSPACE: return "workspace too small";
     case PKV_EHIP: return "HIP launch error";
     case PKV_ENOSPACE: return "no free blocks";
+    case PKV_ESCRATCH: return "shape needs more than the static scratch";
   }
   return "unknown status";
 }
@@ -286,6 +311,29 @@ int paged_attention_append(void* out, const void* q, const void* k_new, const vo
   return attention_impl(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, num_seqs,
                         num_q_tokens, max_blocks_per_seq, max_query_len, num_q_heads, num_kv_heads, head_dim,
                         num_blocks, block_size, scale, false, 1.f, 1.f, workspace, workspace_bytes, stream,
+                        k_new, v_new, slot_mapping, true);
+}
+
+int paged_attention_append_noalloc(void* out, const void* q, const void* k_new, const void* v_new,
+                                   const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                                   const int32_t* block_tables, const int32_t* seq_lens,
+                                   const int32_t* query_start_loc, int32_t num_seqs, int64_t num_q_tokens,
+                                   int32_t max_blocks_per_seq, int32_t max_query_len, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                                   int32_t block_size, float scale, void* stream) {
+  // the size this shape needs (argument checks of the query form included)
+  size_t need = 0;
+  int st = attention_impl(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, num_seqs, num_q_tokens,
+                          max_blocks_per_seq, max_query_len, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                          block_size, scale, false, 1.f, 1.f, nullptr, &need, stream);
+  if (st != PKV_OK) return st;
+  if (need > kNoallocScratchBytes) return PKV_ESCRATCH;
+  void* ws = noalloc_scratch_for_current_device();
+  if (!ws) return PKV_EHIP;
+  size_t have = kNoallocScratchBytes;
+  return attention_impl(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, num_seqs,
+                        num_q_tokens, max_blocks_per_seq, max_query_len, num_q_heads, num_kv_heads, head_dim,
+                        num_blocks, block_size, scale, false, 1.f, 1.f, ws, &have, stream,
                         k_new, v_new, slot_mapping, true);
 }
 

@@ -15,7 +15,7 @@ from paged_kv_cache_tables_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pagedkv.h")
 
-PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE = 0, -1, -2, -3
+PKV_OK, PKV_EINVAL, PKV_EUNSUPPORTED, PKV_EWORKSPACE, PKV_ESCRATCH = 0, -1, -2, -3, -6
 
 
 @pytest.fixture(scope="module")
@@ -102,8 +102,8 @@ def test_workspace_query_and_size(lib):
     assert pkv.workspace_bytes(4, 4, 2, 64, 4, 16, max_query_len=500) == n.value
     assert pkv.workspace_bytes(400, 4, 2, 64, 4, 16) > n.value
     assert pkv.workspace_bytes(4, 4, 2, 64, 4000, 16) > n.value
-    # D 128: 34 MB of partials for any batch
-    assert pkv.workspace_bytes(256, 64, 8, 128, 512, 16) < 40 << 20
+    # D 128: 34 MB of partials for any batch; every task configuration fits the static scratch
+    assert pkv.workspace_bytes(256, 64, 8, 128, 512, 16) < pkv.NOALLOC_SCRATCH_BYTES
 
 
 @pytest.mark.parametrize("over,expect", [
@@ -134,8 +134,28 @@ def test_paged_attention_checks_pointers_before_launch(lib):
     assert lib.paged_attention(*args) == PKV_OK                         # empty batch: no launch
 
 
+def test_noalloc_rejects_before_any_device_call(lib):
+    """paged_attention_append_noalloc checks its arguments and the scratch its shape needs on the
+    host: invalid shapes and shapes beyond the static scratch return before any HIP call."""
+    def call(**over):
+        a = dict(num_seqs=256, T=256, max_blocks=512, max_query_len=1, Hq=64, Hkv=8, D=128, NB=1 << 16,
+                 bs=16, scale=0.088)
+        a.update(over)
+        return lib.paged_attention_append_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                  a["num_seqs"], a["T"], a["max_blocks"], a["max_query_len"],
+                                                  a["Hq"], a["Hkv"], a["D"], a["NB"], a["bs"], a["scale"], None)
+    # 4096 sequences of up to 131072 tokens: the prefill work list alone exceeds the scratch
+    need = pkv.workspace_bytes(4096, 64, 8, 128, 8192, 16, 1)
+    assert need > pkv.NOALLOC_SCRATCH_BYTES
+    assert call(num_seqs=4096, T=4096, max_blocks=8192) == PKV_ESCRATCH
+    assert call(Hq=6, Hkv=4) == PKV_EINVAL
+    assert call(D=96) == PKV_EUNSUPPORTED
+    assert call(scale=float("inf")) == PKV_EINVAL
+    assert pkv.workspace_bytes(64, 32, 8, 128, 256, 16, 1) <= pkv.NOALLOC_SCRATCH_BYTES
+
+
 def test_status_strings(lib):
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert lib.pkv_status_string(code).decode() == _lib.STATUS[code]
 
 
