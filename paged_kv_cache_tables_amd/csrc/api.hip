@@ -24,8 +24,24 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 struct WsLayout {
   int64_t max_splits;
   int64_t plan_capacity;
-  size_t o_off, m_off, l_off, nparts_off, count_off, items_off, total;
+  int64_t share_seqs, mem_rows0;
+  size_t o_off, m_off, l_off, nparts_off, memrec_off, count_off, items_off, total;
 };
+
+// The largest number of sequences a call may have for its decode rows to be checked for shared
+// prefix blocks: each decode wave hashes the sequences' first blocks in its own tile buffer (at
+// most a quarter full), a workgroup builds the plan in its tile buffers (2 hash slots and 8 ints
+// per sequence, plus a few per thread), and keeps it after them in LDS, where the (8 / group)
+// workgroups a compute unit holds must still fit in its 160 KiB.
+int share_cap(int D, int group) {
+  const int tile_ints = 64 * (D / 8) * 4;        // ints of one wave's tile buffer
+  int cap = std::min(pkv::kShareMaxSeqs, tile_ints / 4);
+  while (cap > 0 && 12 * cap + group * 64 + 16 > group * tile_ints) cap /= 2;
+  while (cap > 0 && (size_t)(8 / group) * ((size_t)group * tile_ints + pkv::share_plan_ints(cap)) * 4 >
+                        (size_t)160 * 1024)
+    cap /= 2;
+  return cap;
+}
 
 // Rows per sequence that are computed as decode rows: q_s x G (row, head) columns fill
 // at most the 16 columns of the decode kernel's score product.
@@ -53,27 +69,40 @@ int decode_waves_for_current_device() {
 }
 
 // Split-K partials of decode rows and the pieces' records, then the prefill planner's
-// count and work list.  A decode workgroup leaves at most two partial pieces (the first
-// and the last of its share), each a row of 16 columns per wave, so the partials take
-// decode_waves x 2 x 16 rows of D + 2 floats whatever the batch.  The rest depends on
-// (num_seqs, Hq, Hkv, max_blocks, bs).  A decode wave's share is at least kMinShareTokens
-// keys, so a (sequence, head) of at most max_blocks * bs keys is cut into at most
+// count and work list.  A decode workgroup leaves at most two partial pieces that do not
+// cover their segment (the first and the last of its share), each a row of 16 columns per
+// wave: decode_waves x 2 x 16 rows of D + 2 floats whatever the batch.  Calls checked for
+// shared prefixes (share_seqs = num_seqs) add two rows per (sequence, query head) and a
+// record per sequence.  A decode wave's share is at least kMinShareTokens keys, so a
+// (sequence, head) of at most max_blocks * bs keys is cut into at most
 // ceil(max_tokens / kMinShareTokens) + 1 pieces (max_splits; it picks the merge form).
-WsLayout workspace_layout(int num_seqs, int Hq, int Hkv, int D, int max_blocks, int bs, int decode_waves) {
+WsLayout workspace_layout(int num_seqs, int Hq, int Hkv, int D, int max_blocks, int bs, int decode_waves,
+                          int group) {
   WsLayout w{};
   const int64_t max_tokens = (int64_t)max_blocks * bs;
   w.max_splits = (max_tokens + kMinShareTokens - 1) / kMinShareTokens + 1;
   const int rows = pkv::kPrefillPairs / (Hq / Hkv);
   w.plan_capacity = (int64_t)num_seqs * ((max_tokens + rows - 1) / rows);
-  const size_t cells = (size_t)decode_waves * 2 * 16;
+  w.share_seqs = num_seqs <= share_cap(D, group) ? num_seqs : 0;
+  w.mem_rows0 = (int64_t)decode_waves * 2 * 16;
+  const size_t prows = (size_t)w.mem_rows0 + 2 * (size_t)w.share_seqs * Hq;
+  const size_t nseg = (size_t)num_seqs + (size_t)w.share_seqs;
   w.o_off = 0;
-  w.m_off = round_up(cells * D * sizeof(float), 256);
-  w.l_off = w.m_off + round_up(cells * sizeof(float), 256);
-  w.nparts_off = w.l_off + round_up(cells * sizeof(float), 256);
-  w.count_off = w.nparts_off + round_up((size_t)num_seqs * Hkv * 2 * sizeof(int), 256);
+  w.m_off = round_up(prows * D * sizeof(float), 256);
+  w.l_off = w.m_off + round_up(prows * sizeof(float), 256);
+  w.nparts_off = w.l_off + round_up(prows * sizeof(float), 256);
+  w.memrec_off = w.nparts_off + round_up(nseg * Hkv * 2 * sizeof(int), 256);
+  w.count_off = w.memrec_off + round_up((size_t)w.share_seqs * 2 * sizeof(int), 256);
   w.items_off = w.count_off + 256;
   w.total = w.items_off + round_up((size_t)w.plan_capacity * 8, 256);
   return w;
+}
+
+// KV heads a decode workgroup takes together: the largest power of two <= 8 dividing Hkv.
+int decode_group_for(int Hkv) {
+  int g = 1;
+  while (g < pkv::kMaxDecodeGroup && Hkv % (2 * g) == 0) g *= 2;
+  return g;
 }
 
 // Static scratch of paged_attention_append_noalloc: the workspace of one call, in a device
@@ -206,8 +235,9 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
     return PKV_EUNSUPPORTED;
   if (num_seqs > 65535 || num_q_heads > 65535) return PKV_EUNSUPPORTED;   // 16-bit sequence and head counts
   const int decode_waves = decode_waves_for_current_device();
+  const int group = decode_group_for(num_kv_heads);
   const WsLayout ws = workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
-                                       block_size, decode_waves);
+                                       block_size, decode_waves, group);
   if (ws.max_splits > 65535 || ws.plan_capacity > INT32_MAX) return PKV_EUNSUPPORTED;
   // decode work units (sequence, KV head, 64-token tile) are counted in 32 bits
   if ((int64_t)num_seqs * num_kv_heads * (((int64_t)max_blocks_per_seq * block_size + 63) / 64) > INT32_MAX)
@@ -258,8 +288,7 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
   }
   p.decode_waves = decode_waves;
   // the KV heads a decode workgroup reads together: the largest power of two <= 8 dividing Hkv
-  p.decode_group = 1;
-  while (p.decode_group < pkv::kMaxDecodeGroup && num_kv_heads % (2 * p.decode_group) == 0) p.decode_group *= 2;
+  p.decode_group = group;
   p.decode_max_q = decode_rows(num_q_heads, num_kv_heads, max_query_len);
   p.min_share_tiles = kMinShareTokens / 64;
   p.max_splits = ws.max_splits;
@@ -268,6 +297,14 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
   p.ws_m = (float*)(wsb + ws.m_off);
   p.ws_l = (float*)(wsb + ws.l_off);
   p.ws_nparts = (int2*)(wsb + ws.nparts_off);
+  p.mem_rows0 = ws.mem_rows0;
+  p.share_seqs = (int)ws.share_seqs;
+  p.share_hash_slots = 2;
+  while (p.share_hash_slots < 2 * p.share_seqs) p.share_hash_slots *= 2;
+  p.plan_memrec = (int2*)(wsb + ws.memrec_off);
+  p.plan_bin_shift = 0;
+  while ((((int64_t)max_blocks_per_seq * block_size + 63) / 64 >> p.plan_bin_shift) >= pkv::kPlanBinsHost)
+    ++p.plan_bin_shift;
   p.plan_count = (int*)(wsb + ws.count_off);
   p.plan_items = (int2*)(wsb + ws.items_off);
   p.plan_capacity = (int)ws.plan_capacity;

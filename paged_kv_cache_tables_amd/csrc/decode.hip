@@ -20,14 +20,16 @@
 // accumulation and the vector ALUs are left with the softmax.
 //
 // Layout (gfx950, v_mfma_f32_16x16x32_bf16):
-//   * Partition: the decode rows' work is cut into units (sequence, group of
-//     KV heads, 64-token tile), in that order.  The grid has one wave per
-//     resident wave slot of the device; a workgroup holds one wave per KV head
-//     of a group (up to 8) and takes an equal consecutive share of units,
-//     walked as pieces of consecutive (sequence, group) segments.  The waves
-//     of a workgroup read the same slots for different heads, and a slot's
-//     heads sit side by side in the pool, so the DRAM rows behind each slot
-//     are read together.
+//   * Partition (built by the plan kernel, plan.hip): the decode rows' work is
+//     cut into units (segment, group of KV heads, 64-token tile), in that
+//     order.  A segment is a sequence's own tiles, or the tiles a group of
+//     sequences maps to the same physical blocks (a shared prefix) for a block
+//     of 16 query columns of its members.  The grid has one wave per resident
+//     wave slot of the device; a workgroup holds one wave per KV head of a
+//     group (up to 8) and takes an equal consecutive share of units, walked as
+//     pieces of consecutive segments.  The waves of a workgroup read the same
+//     slots for different heads, and a slot's heads sit side by side in the
+//     pool, so the DRAM rows behind each slot are read together.
 //   * Loads are fully coalesced: 16 lanes read one 256-byte row (16 bytes each),
 //     4 rows per instruction; the pool block of each instruction is
 //     wave-uniform (scalar base).  K and V of a tile arrive in registers.
@@ -46,49 +48,290 @@
 //   * Fused append: positions that are this call's new tokens are read from the
 //     new rows (k_new / v_new) instead of the pools, which the merge launch
 //     fills afterwards.
-//   A piece that covers its whole (sequence, head) writes bf16 output directly;
-//   otherwise fp32 partials (O, m, l) go to the workspace for the merge kernel.
+//   * Shared prefixes: a group piece takes its 16 columns from 16 / G member
+//     sequences (one decode row each) and reads the shared tiles through the
+//     leader's table.
+//   A piece that covers a whole private segment of a sequence in no group
+//   writes bf16 output directly; every other piece writes fp32 partials
+//   (O, m, l) to the workspace, which the merge kernel combines.
 #include <algorithm>
 #include <climits>
 
 #include "common.h"
 #include "kernels.h"
 #include "planner.h"
+#include "rows.h"
 
 namespace pkv {
 
 namespace {
 
-constexpr int kTile = 64;        // tokens per tile
-
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef short short8v __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) short4v lds_short4;
 
-// First query row, row count, key count and 64-token tiles of sequence s when its rows
-// are decode rows -- 1 <= q_s <= decode_max_q, so that its q_s x G (row, head) columns fit
-// the 16 columns of the score product -- and no tiles otherwise.
-struct SeqInfo {
-  int row0, q, len, tiles;
+// ---------------------------------------------------------------------------------------
+// Shared prefixes.  Sequences of a batch can map the same physical blocks for a common
+// prefix ("Under the Hood: PagedAttention", prefix sharing: one cached copy, several block
+// tables pointing at it -- Text Generation Inference page; the radix prefix cache of the
+// text-generation-inference v3 walkthrough builds such tables).  Attending that prefix once
+// per sequence re-reads the same K/V.  Every decode wave first checks, in its own LDS tile
+// buffer, whether two decode sequences (one query row each) start with the same block.  If
+// none do, the partition below is the plain per-sequence one.  If some do, every workgroup
+// builds the same sharing plan in LDS (the tile buffers as scratch, a small region after
+// them for the result): the sequences with a common first block form a group under the
+// first of them (the leader); each member's block table is compared with the leader's,
+// entry by entry, up to the cached full 64-token tiles of both; the group's shared run is
+// the shortest such run among the members that share at least one tile.  Those tiles are
+// then attended once per block of 16 query columns (16 / G members): group segments, read
+// through the leader's table, placed after the sequences' own (private) segments, which
+// skip them.  The merge kernel combines a member's private and group pieces.
+// ---------------------------------------------------------------------------------------
+
+// The plan's result, kept in LDS after the tile buffers for the whole kernel, for S
+// sequences (Sr = S rounded up to a multiple of 4): [hdr 4][tiles skipped by each sequence
+// Sr][members Sr][groups (leader, shared tiles, first member, members) Sr / 2 int4][group
+// segment unit offsets Sr + 4][group segment (group, block) Sr int2] = 7 Sr + 8 ints.
+struct SharePlan {
+  int* hdr;         // [0] groups, [1] group segments, [2] units of all group segments
+  int* tofs;        // per sequence: leading tiles attended by its group (0: not a member)
+  int* members;     // member sequences, grouped, in sequence order within a group
+  int4* grp;        // per group: (leader, shared tiles, first member slot, members)
+  int* cboff;       // per group segment: first unit, relative to the first group unit
+  int2* cbrec;      // per group segment: (group, column block within the group)
+  __device__ SharePlan(int* base, int S) {
+    const int Sr = (S + 3) & ~3;
+    hdr = base;
+    tofs = hdr + 4;
+    members = tofs + Sr;
+    grp = reinterpret_cast<int4*>(members + Sr);  // 16-byte aligned: 4 + 2 Sr ints, Sr % 4 == 0
+    cboff = reinterpret_cast<int*>(grp + Sr / 2);
+    cbrec = reinterpret_cast<int2*>(cboff + Sr + 4);
+  }
 };
-__device__ __forceinline__ SeqInfo seq_info(const AttnParams& p, int s) {
-  const int row0 = p.qsl[s];
-  const int q = p.qsl[s + 1] - row0;
-  const int len = min(p.seq_lens[s], p.max_blocks * p.bs);   // clamp a length the table cannot map
-  if (q < 1 || q > p.decode_max_q || row0 < 0 || row0 + q > p.num_q_tokens || len <= 0)
-    return SeqInfo{row0, 0, 0, 0};
-  return SeqInfo{row0, q, len, (len + kTile - 1) / kTile};
+
+// Exclusive prefix sum of one int per thread over the workgroup; `total` gets the sum.
+__device__ int block_excl_scan(int v, int* wave_tot, int& total) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave, nw = blockDim.x / kWave;
+  const int incl = wave_incl_scan(v);
+  if (lane == kWave - 1) wave_tot[w] = incl;
+  __syncthreads();
+  int before = 0, tot = 0;
+  for (int i = 0; i < nw; ++i) {
+    const int x = wave_tot[i];
+    before += i < w ? x : 0;
+    tot += x;
+  }
+  __syncthreads();
+  total = tot;
+  return before + incl - v;
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int d = 1; d < kWave; d *= 2) {
-    const int y = __shfl_up(v, d, kWave);
-    if (lane >= d) v += y;
+// Builds the sharing plan with every thread of the workgroup (each workgroup builds the same
+// plan).  scratch: the tile buffers, at least 9 S + 2 hash_slots + 16 ints.
+// NG = KV-head groups (units per tile).  Workgroup 0 also writes each sequence's group record
+// for the merge kernel.
+__device__ void build_share_plan(const AttnParams& p, int* scratch, const SharePlan& P, int NG, int G) {
+  const int S = p.num_seqs, t = threadIdx.x, T = blockDim.x;
+  const int HS = p.share_hash_slots;              // a power of two >= 2 S
+  const int nblocks = p.num_blocks > INT_MAX ? INT_MAX : (int)p.num_blocks;
+  const int bpt = kTile / p.bs;                   // pool blocks per tile
+  int* hkey = scratch;                            // first block ids, -1 = empty
+  int* hval = hkey + HS;                          // smallest sequence with that first block
+  int* leader = hval + HS;                        // leader of a candidate, else -1
+  int* tiles = leader + S;                        // hash slot, then tiles shared with the leader
+  int* cnt = tiles + S;                           // per leader: candidates, then first group segment
+  int* dtiles = cnt + S;                          // decode tiles of each sequence
+  int* nmem = dtiles + S;                         // per leader: members
+  int* gt = nmem + S;                             // per leader: shared tiles of the group
+  int* mis = gt + S;                              // first block that differs from the leader's
+  int* membase = mis + S;                         // per leader: first member slot
+  int* cmp_list = membase + S;                    // [S] candidates whose tables are compared
+  int* wave_tot = cmp_list + S;                   // [T / 64]
+
+  // A: candidates (one decode row, at least one cached full tile -- its decode tiles minus
+  // the tile of its newest token) keyed by their first block
+  for (int i = t; i < HS; i += T) { hkey[i] = -1; hval[i] = INT_MAX; }
+  for (int s = t; s < S; s += T) { leader[s] = -1; cnt[s] = 0; nmem[s] = 0; gt[s] = INT_MAX; mis[s] = INT_MAX; }
+  __syncthreads();
+  for (int s = t; s < S; s += T) {
+    const int b0 = p.block_tables[(size_t)s * p.max_blocks];
+    const SeqInfo si = seq_info(p, s);
+    dtiles[s] = si.tiles;
+    if (si.q != 1 || si.tiles < 2 || (unsigned)b0 >= (unsigned)nblocks) continue;
+    unsigned h = ((unsigned)b0 * 2654435761u) & (unsigned)(HS - 1);
+    for (int probe = 0; probe < HS; ++probe) {    // at most S keys in HS >= 2 S slots
+      const int prev = atomicCAS(&hkey[h], -1, b0);
+      if (prev == -1 || prev == b0) break;
+      h = (h + 1) & (unsigned)(HS - 1);
+    }
+    atomicMin(&hval[h], s);
+    tiles[s] = (int)h;
+    leader[s] = -2;
   }
-  return v;
+  __syncthreads();
+  for (int s = t; s < S; s += T) {
+    if (leader[s] != -2) continue;
+    const int l = hval[tiles[s]];
+    leader[s] = l;
+    atomicAdd(&cnt[l], 1);
+  }
+  __syncthreads();
+  // B: tiles each candidate shares with its leader
+  for (int s = t; s < S; s += T) {
+    const int l = leader[s];
+    tiles[s] = (l >= 0 && cnt[l] >= 2) ? min(dtiles[s], dtiles[l]) - 1 : 0;
+  }
+  __syncthreads();
+  // the candidates to compare (not leaders, at least one tile in common by length), listed in
+  // cmp_list; then each wave takes batches of kCmpBatch of them, lane j comparing table entry
+  // j0 + j of each (blocks 1 .. tiles * bpt - 1; block 0 is equal by construction), all of a
+  // round's loads issued before any is checked
+  int ncmp = 0;
+  for (int c0 = 0; c0 < S; c0 += T) {
+    const int s = c0 + t;
+    const bool want = s < S && leader[s] >= 0 && leader[s] != s && tiles[s] > 0;
+    int tot;
+    const int idx = ncmp + block_excl_scan(want ? 1 : 0, wave_tot, tot);
+    if (want) cmp_list[idx] = s;
+    ncmp += tot;
+  }
+  __syncthreads();
+  {
+    constexpr int kCmpBatch = 16;
+    const int lane = t & (kWave - 1), wv = t / kWave, nw = T / kWave;
+    for (int base = wv * kCmpBatch; base < ncmp; base += nw * kCmpBatch) {
+      int sm[kCmpBatch], lm[kCmpBatch], nbm[kCmpBatch];
+      unsigned done = 0;
+#pragma unroll
+      for (int k = 0; k < kCmpBatch; ++k) {
+        const int i = base + k;
+        sm[k] = i < ncmp ? cmp_list[i] : 0;
+        lm[k] = i < ncmp ? leader[sm[k]] : 0;
+        nbm[k] = i < ncmp ? tiles[sm[k]] * bpt : 0;
+        if (nbm[k] <= 1) done |= 1u << k;
+      }
+      for (int j0 = 1; done != (1u << kCmpBatch) - 1; j0 += kWave) {
+        int va[kCmpBatch], vb[kCmpBatch];
+#pragma unroll
+        for (int k = 0; k < kCmpBatch; ++k) {
+          const int j = j0 + lane;
+          const bool act = !(done >> k & 1) && j < nbm[k];
+          va[k] = act ? p.block_tables[(size_t)sm[k] * p.max_blocks + j] : 0;
+          vb[k] = act ? p.block_tables[(size_t)lm[k] * p.max_blocks + j] : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < kCmpBatch; ++k) {
+          if (done >> k & 1) continue;
+          const unsigned long long d = __builtin_amdgcn_ballot_w64(j0 + lane < nbm[k] && va[k] != vb[k]);
+          if (d) {
+            if (lane == 0) mis[sm[k]] = j0 + (int)__builtin_ctzll(d);
+            done |= 1u << k;
+          } else if (j0 + kWave >= nbm[k]) {
+            done |= 1u << k;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (int s = t; s < S; s += T)
+    if (leader[s] >= 0 && leader[s] != s && mis[s] != INT_MAX) tiles[s] = min(tiles[s], mis[s] / bpt);
+  __syncthreads();
+  // C: a group = its candidates sharing at least one tile (the leader among them); its shared
+  // run is the shortest of theirs
+  for (int s = t; s < S; s += T) {
+    const int l = leader[s];
+    if (l >= 0 && tiles[s] >= 1) {
+      atomicMin(&gt[l], tiles[s]);
+      atomicAdd(&nmem[l], 1);
+    }
+  }
+  __syncthreads();
+  auto is_member = [&](int s) {
+    const int l = leader[s];
+    return l >= 0 && tiles[s] >= 1 && nmem[l] >= 2;
+  };
+  // D: groups in leader order; each group's column blocks are its segments
+  int ngroups = 0, ncb = 0, nmembers = 0;
+  for (int c0 = 0; c0 < S; c0 += T) {
+    const int s = c0 + t;
+    const bool lead = s < S && leader[s] == s && nmem[s] >= 2;
+    const int ng = lead ? nmem[s] : 0;
+    const int nc = (ng * G + 15) / 16;
+    int tg, tc, tm;
+    const int gi = ngroups + block_excl_scan(lead ? 1 : 0, wave_tot, tg);
+    const int cbb = ncb + block_excl_scan(nc, wave_tot, tc);
+    const int mb = nmembers + block_excl_scan(ng, wave_tot, tm);
+    if (lead) {
+      cnt[s] = cbb;
+      membase[s] = mb;
+      P.grp[gi] = make_int4(s, gt[s], mb, ng);
+      for (int cb = 0; cb < nc; ++cb) P.cbrec[cbb + cb] = make_int2(gi, cb);
+    }
+    ngroups += tg;
+    ncb += tc;
+    nmembers += tm;
+  }
+  __syncthreads();
+  // members in sequence order within each group: wave 0 walks the sequences 64 at a time,
+  // ranking the members of each group present with a ballot and a running count per leader
+  // (in mis, free by now); a member's columns are (rank G .. + G - 1) of its group, in column
+  // block (rank G) / 16
+  for (int s = t; s < S; s += T) mis[s] = 0;     // running member count per leader
+  __syncthreads();
+  if (t < kWave) {
+    for (int c0 = 0; c0 < S; c0 += kWave) {
+      const int s = c0 + t;
+      const int l = (s < S && is_member(s)) ? leader[s] : -1;
+      unsigned long long left = __builtin_amdgcn_ballot_w64(l >= 0);
+      while (left) {
+        const int src = (int)__builtin_ctzll(left);
+        const int lg = __shfl(l, src, kWave);
+        const unsigned long long m = __builtin_amdgcn_ballot_w64(l == lg);
+        const int before = mis[lg];
+        if (l == lg) {
+          const int rank = before + (int)__builtin_popcountll(m & ((1ull << t) - 1));
+          tiles[s] = -1 - rank;                  // the rank, marked (tiles is no longer needed)
+        }
+        wave_lds_sync();
+        if (t == src) mis[lg] = before + (int)__builtin_popcountll(m);
+        wave_lds_sync();
+        left &= ~m;
+      }
+    }
+  }
+  __syncthreads();
+  for (int s = t; s < S; s += T) {
+    int2 rec = make_int2(-1, 0);
+    int skip = 0;
+    if (tiles[s] < 0) {                          // a member: tiles holds -1 - rank
+      const int l = leader[s], rank = -1 - tiles[s];
+      P.members[membase[l] + rank] = s;
+      rec = make_int2(S + cnt[l] + rank * G / 16, (rank * G) % 16);
+      skip = gt[l];
+    }
+    P.tofs[s] = skip;
+    if (blockIdx.x == 0) p.plan_memrec[s] = rec;
+  }
+  __syncthreads();
+  // group segment offsets (units: NG per shared tile)
+  int run = 0;
+  for (int c0 = 0; c0 < ncb; c0 += T) {
+    const int k = c0 + t;
+    const int u = k < ncb ? NG * P.grp[P.cbrec[k].x].y : 0;
+    int tt;
+    const int off = run + block_excl_scan(u, wave_tot, tt);
+    if (k < ncb) P.cboff[k] = off;
+    run += tt;
+  }
+  if (t == 0) {
+    P.cboff[ncb] = run;
+    P.hdr[0] = ngroups;
+    P.hdr[1] = ncb;
+    P.hdr[2] = run;
+  }
+  __syncthreads();
 }
 
 // MULTI: some sequence may have several decode rows (decode_max_q > 1); otherwise every
@@ -121,50 +364,132 @@ void decode_kernel(AttnParams p) {
   const int WPG = p.decode_group;                // KV heads (waves) per workgroup; divides Hkv
   const int NG = Hkv / WPG;                      // head groups
 
-  // ---- the partition: units (s, head group, tile) in that order, an equal share per workgroup ----
-  // The waves of a workgroup take the same units for the heads of one group, so the heads'
-  // rows of each pool slot (adjacent in memory) are read at the same time.  Lane l sums the
-  // tiles of sequences [l c, (l + 1) c); a wave scan gives each lane the units before its
-  // chunk.  Unit counts fit in 32 bits (checked by the host).
-  const int c_per = (p.num_seqs + kWave - 1) / kWave;
+  // ---- the partition: units (segment, head group, tile) in that order, an equal share per
+  // workgroup.  Segments: each sequence's own tiles (those its sharing group does not attend
+  // for it), then the sharing groups' column blocks.  The waves of a workgroup take the same
+  // units for the heads of one group, so the heads' rows of each pool slot (adjacent in memory)
+  // are read at the same time.  Lane l sums the tiles of sequences [l c, (l + 1) c); a wave
+  // scan gives each lane the units before its chunk.  Unit counts fit in 32 bits (checked by
+  // the host). ----
+  const int S = p.num_seqs;
+  const int c_per = (S + kWave - 1) / kWave;
+  // sharing check: the candidates' first blocks in a hash table (share_hash_slots >= 2 S
+  // entries, a power of two) at the start of this wave's tile buffer
+  const bool detect = p.share_seqs > 0;
+  int* whash = reinterpret_cast<int*>(&tile[0][0]);
+  const int HS = p.share_hash_slots;
+  if (detect) {
+    for (int i = lane; i < HS / 4; i += kWave) reinterpret_cast<uint4*>(whash)[i] = make_uint4(~0u, ~0u, ~0u, ~0u);
+    wave_lds_sync();
+  }
+  const int nblocks_i = p.num_blocks > 0x7fffffff ? 0x7fffffff : (int)p.num_blocks;
   int my_tiles = 0;
+  bool dup = false;
   SeqInfo first{0, 0, 0, 0};                     // this lane's first sequence
-  for (int i = 0; i < c_per; ++i) {
-    const int s = lane * c_per + i;
-    if (s < p.num_seqs) {
-      const SeqInfo si = seq_info(p, s);
-      if (i == 0) first = si;
-      my_tiles += si.tiles;
+  // the lane's sequences in batches, every load of a batch issued before any is used
+  constexpr int kSeqBatch = 8;
+  for (int i0 = 0; i0 < c_per; i0 += kSeqBatch) {
+    SeqInfo si[kSeqBatch];
+    int b0[kSeqBatch];
+#pragma unroll
+    for (int k = 0; k < kSeqBatch; ++k) {
+      const int s = lane * c_per + i0 + k;
+      const bool ok = i0 + k < c_per && s < S;
+      si[k] = ok ? seq_info(p, s) : SeqInfo{0, 0, 0, 0};
+      b0[k] = (ok && detect) ? p.block_tables[(size_t)s * p.max_blocks] : -1;
+    }
+    if (i0 == 0) first = si[0];
+#pragma unroll
+    for (int k = 0; k < kSeqBatch; ++k) {
+      my_tiles += si[k].tiles;
+      if (detect && si[k].q == 1 && si[k].tiles >= 2 && (unsigned)b0[k] < (unsigned)nblocks_i) {
+        unsigned h = ((unsigned)b0[k] * 2654435761u) & (unsigned)(HS - 1);
+        for (int probe = 0; probe < HS; ++probe) {   // at most S keys in HS >= 2 S slots
+          const int prev = atomicCAS(&whash[h], -1, b0[k]);
+          if (prev == -1) break;
+          if (prev == b0[k]) { dup = true; break; }
+          h = (h + 1) & (unsigned)(HS - 1);
+        }
+      }
+    }
+  }
+  // every wave of the workgroup finds the same answer (the same keys)
+  const bool sharing = detect && __builtin_amdgcn_ballot_w64(dup) != 0;
+  if (detect && !sharing && w == 0)              // no group: the merge kernel sees no member
+    for (int i = threadIdx.x; i < S; i += blockDim.x) p.plan_memrec[i] = make_int2(-1, 0);
+  const SharePlan P(reinterpret_cast<int*>(lds_tiles + (size_t)WPG * kTile * CH), S);
+  if (sharing) {
+    __syncthreads();                             // every wave is done with its own table
+    build_share_plan(p, reinterpret_cast<int*>(lds_tiles), P, NG, G);
+    for (int i = 0; i < c_per; ++i) {
+      const int s = lane * c_per + i;
+      if (s < S) my_tiles -= P.tofs[s];
     }
   }
   const int incl = wave_incl_scan(my_tiles);
-  const int total_units = uniform(__shfl(incl, kWave - 1, kWave) * NG);
+  const int priv_units_total = uniform(__shfl(incl, kWave - 1, kWave) * NG);   // NG x private tiles
+  const int total_units = priv_units_total + (sharing ? uniform(P.hdr[2]) : 0);
   if (total_units == 0) return;
   const int nwg = p.decode_waves / WPG;          // workgroups of the grid
   const int share = uniform(max(p.min_share_tiles, (total_units + nwg - 1) / nwg));
   if (w >= (total_units + share - 1) / share) return;   // fewer shares than workgroups
   const int x0 = w * share;
   const int x1 = min(x0 + share, total_units);
-  // the lane whose chunk holds unit x0, then the sequence inside that chunk
-  const int excl_units = (incl - my_tiles) * NG;
-  const unsigned long long hit = __builtin_amdgcn_ballot_w64(excl_units <= x0 && x0 < incl * NG);
-  const int src = (int)__builtin_ctzll(hit);     // nonempty: x0 < total_units
-  int s = uniform(src * c_per);
-  int seg_a = uniform(__shfl(excl_units, src, kWave));   // first unit of sequence s
-  int cur_row0 = uniform(__shfl(first.row0, src, kWave));
-  int cur_q = uniform(__shfl(first.q, src, kWave));
-  int cur_len = uniform(__shfl(first.len, src, kWave));
-  int nt = uniform(__shfl(first.tiles, src, kWave));
-  auto next_seq = [&]() {
-    seg_a += NG * nt;
-    s = uniform(s + 1);
-    const SeqInfo si = seq_info(p, s);
-    cur_row0 = uniform(si.row0);
-    cur_q = uniform(si.q);
-    cur_len = uniform(si.len);
-    nt = uniform(si.tiles);
+
+  // The current segment.  Private: sequence s, its rows (cur_row0, cur_q) and length, tiles
+  // [t_off, t_off + nt).  Group column block k (segment S + k): s = the group's leader (whose
+  // table is read), cur_q = -1 - k, cur_len = the shared keys, nt = the shared tiles, t_off = 0;
+  // the block's members come from the plan in LDS when a piece needs them.
+  int s = 0, seg_a = 0, cur_row0 = 0, cur_q = 0, cur_len = 0, nt = 0, t_off = 0;
+  auto load_cb = [&](int k) {
+    const int4 gr = P.grp[P.cbrec[k].x];
+    s = uniform(gr.x);
+    nt = uniform(gr.y);
+    cur_len = nt * kTile;
+    cur_q = -1 - k;
+    cur_row0 = 0;
+    t_off = 0;
   };
-  while (x0 >= seg_a + NG * nt && s + 1 < p.num_seqs) next_seq();
+  if (x0 < priv_units_total) {
+    // the lane whose chunk holds unit x0, then the sequence inside that chunk
+    const int excl_units = (incl - my_tiles) * NG;
+    const unsigned long long hit = __builtin_amdgcn_ballot_w64(excl_units <= x0 && x0 < incl * NG);
+    const int src = (int)__builtin_ctzll(hit);   // nonempty: x0 < priv_units_total
+    s = uniform(src * c_per);
+    seg_a = uniform(__shfl(excl_units, src, kWave));   // first unit of sequence s
+    cur_row0 = uniform(__shfl(first.row0, src, kWave));
+    cur_q = uniform(__shfl(first.q, src, kWave));
+    cur_len = uniform(__shfl(first.len, src, kWave));
+    t_off = sharing ? uniform(P.tofs[s]) : 0;
+    nt = uniform(__shfl(first.tiles, src, kWave)) - t_off;
+  } else {
+    // a group segment: the last one whose first unit is <= x0
+    const int y = x0 - priv_units_total;
+    int lo = 0, hi = uniform(P.hdr[1]) - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (uniform(P.cboff[mid]) <= y) lo = mid; else hi = mid - 1;
+    }
+    seg_a = priv_units_total + uniform(P.cboff[lo]);
+    load_cb(lo);
+  }
+  auto next_seg = [&]() {
+    seg_a += NG * nt;
+    if (cur_q < 0) {                             // the next group segment
+      load_cb(-cur_q);
+    } else if (s + 1 < S) {                      // the next sequence
+      s = uniform(s + 1);
+      const SeqInfo si = seq_info(p, s);
+      cur_row0 = uniform(si.row0);
+      cur_q = uniform(si.q);
+      cur_len = uniform(si.len);
+      t_off = sharing ? uniform(P.tofs[s]) : 0;
+      nt = uniform(si.tiles) - t_off;
+    } else {                                     // past the last sequence: the group segments
+      load_cb(0);
+    }
+  };
+  while (cur_q >= 0 && x0 >= seg_a + NG * nt && s + 1 < S) next_seg();
 
   const int n = lane & 15;                       // accumulator column: query head of the group
   const int kg = lane >> 4;                      // k-group / accumulator row group
@@ -177,30 +502,45 @@ void decode_kernel(AttnParams p) {
   const int lrow = lane / CHG, lch = lane % CHG; // this lane's row (within a load) and chunk
   const uint32_t lane_off = (uint32_t)lrow * row_bytes + (uint32_t)lch * 16;
 
-  // One piece: tiles [tb0, tb1) of (sequence s, KV head h), whose units start at unit a.
+  // One piece: tiles [tb0, tb1) of the current segment for KV head h, whose units start at
+  // unit a.
   auto piece = [&](int h, int tb0, int tb1, int a) {
+    const bool grp = cur_q < 0;                  // a group segment's piece
     const int row0 = cur_row0;
     const int L = cur_len;
-    // accumulator column n = (row rr of the sequence's q_s rows, head g of the group); the
-    // row at position L - q_s + rr attends keys 0..lim
-    const int rr = n / G, g = n % G;
-    const bool col_valid = rr < cur_q;
-    const int lim = col_valid ? L - cur_q + rr : L - 1;
-    const int t_begin = tb0 * kTile;
-    const int t_end = min(tb1 * kTile, L);
+    const int g = n % G;
+    // accumulator column n: in a private piece (row rr of the sequence's q_s rows, head g),
+    // the row at position L - q_s + rr attends keys 0..lim; in a group piece (member
+    // cb 16 / G + n / G, head g), whose decode row sees every shared key
+    int qrow = 0, lim = INT_MAX;
+    bool col_valid;
+    if (grp) {
+      const int2 cr = P.cbrec[-1 - cur_q];       // (group, column block)
+      const int4 gr = P.grp[cr.x];               // (leader, shared tiles, first member, members)
+      const int mi = cr.y * (16 / G) + n / G;
+      col_valid = mi < gr.w;
+      if (col_valid) qrow = p.qsl[P.members[gr.z + mi]];
+    } else {
+      const int rr = n / G;
+      col_valid = rr < cur_q;
+      qrow = row0 + (col_valid ? rr : 0);
+      lim = col_valid ? L - cur_q + rr : L - 1;
+    }
+    const int t_begin = uniform((t_off + tb0) * kTile);
+    const int t_end = uniform(min((t_off + tb1) * kTile, L));
     const int* bt_row = p.block_tables + (size_t)s * p.max_blocks;
     const char* kbase = p.k_cache + (size_t)h * D * EB;
     const char* vbase = p.v_cache + (size_t)h * D * EB;
     // positions fresh0 .. L - 1 are this step's tokens; with a fused append they are not in
-    // the pools yet and come from the rows of k_new / v_new instead
-    const int fresh0 = (!F8 && p.k_new != nullptr) ? L - cur_q : INT_MAX;
+    // the pools yet and come from the rows of k_new / v_new instead (never in shared tiles)
+    const int fresh0 = uniform((!F8 && !grp && p.k_new != nullptr) ? L - cur_q : INT_MAX);
     const uint16_t* knew_h = p.k_new + (size_t)h * D;
     const uint16_t* vnew_h = p.v_new + (size_t)h * D;
 
     // ---- Q^T as the B operand: column n, dims ks*32 + kg*8 .. +8 (zero for padding columns) ----
     bf16x8 qreg[KS];
     {
-      const uint16_t* qp = p.q + ((size_t)(row0 + (col_valid ? rr : 0)) * Hq + (size_t)h * G + g) * D;
+      const uint16_t* qp = p.q + ((size_t)qrow * Hq + (size_t)h * G + g) * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         uint4 v = make_uint4(0u, 0u, 0u, 0u);
@@ -223,8 +563,9 @@ void decode_kernel(AttnParams p) {
         dst[j] = (unsigned)b < (unsigned)nblocks ? b : 0;
       }
     };
-    // Coalesced tile load: load i covers rows RPI*i .. RPI*i + RPI - 1 (one pool block).  A
-    // tile that holds fresh positions takes those rows from the new rows instead (lane by lane).
+    // Coalesced tile load: load i covers rows RPI*i .. RPI*i + RPI - 1 (one pool block), with the
+    // streaming hint.  A tile that holds fresh positions takes those rows from the new rows
+    // instead (lane by lane).
     auto issue = [&](const char* base, const uint16_t* nbase, const int* bb, uint4* reg, int t0) {
       if (t0 + kTile > fresh0) {
 #pragma unroll
@@ -381,54 +722,73 @@ void decode_kernel(AttnParams p) {
     // (the column's row and head are recomputed here rather than kept live through the loop)
     int n_e = n, kg_e = kg;
     asm volatile("" : "+v"(n_e), "+v"(kg_e));
-    const int rr_e = n_e / G, g_e = n_e % G;
-    const int first_w = a / share;                 // the workgroup holding tile 0 of (s, h)
-    const int nseg = (a + nt - 1) / share - first_w + 1;   // pieces of (s, h)
+    const int g_e = n_e % G;
+    const int qh = h * G + g_e;
+    const int first_w = a / share;                 // the workgroup holding tile 0 of (segment, h)
+    const int nseg = (a + nt - 1) / share - first_w + 1;   // pieces of (segment, h)
     // partial slot: 2 w for the piece that opens this workgroup's share, 2 w + 1 for a later one
     // (only the last piece of a share can be a later partial one)
     const int slot = 2 * w + (a + tb0 != x0 ? 1 : 0);
-    if (tb0 == 0 && lane == 0) p.ws_nparts[(size_t)s * Hkv + h] = make_int2(slot, nseg);
+    const int seg_k = grp ? S - 1 - cur_q : s;   // the segment's record: sequence s, or S + block
+    if (tb0 == 0 && lane == 0) p.ws_nparts[(size_t)seg_k * Hkv + h] = make_int2(slot, nseg);
     float l_tot = l_part + __shfl_xor(l_part, 16, kWave);
     l_tot += __shfl_xor(l_tot, 32, kWave);
-    if (rr_e < cur_q) {
-      const int qh = h * G + g_e;
-      if (nseg == 1) {                           // the whole (s, h): final output
-        const float inv = F8 ? p.v_scale / l_tot : 1.f / l_tot;
-        uint16_t* op = p.out + ((size_t)(row0 + rr_e) * Hq + qh) * D;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) {
-          const uint32_t w0 = (uint32_t)f32_to_bf16_rne(oacc[db][0] * inv) | ((uint32_t)f32_to_bf16_rne(oacc[db][1] * inv) << 16);
-          const uint32_t w1 = (uint32_t)f32_to_bf16_rne(oacc[db][2] * inv) | ((uint32_t)f32_to_bf16_rne(oacc[db][3] * inv) << 16);
-          *reinterpret_cast<uint2*>(op + db * 16 + 4 * kg_e) = make_uint2(w0, w1);
-        }
-      } else {                                   // a partial: row (slot, wave, column) of the workspace
-        const size_t idx = ((size_t)slot * WPG + wv) * 16 + n_e;
-        const float vs = F8 ? p.v_scale : 1.f;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-          *reinterpret_cast<float4*>(p.ws_o + idx * D + db * 16 + 4 * kg_e) =
-              make_float4(oacc[db][0] * vs, oacc[db][1] * vs, oacc[db][2] * vs, oacc[db][3] * vs);
-        if (kg_e == 0) { p.ws_m[idx] = m_run; p.ws_l[idx] = l_tot; }
+    // where column n_e goes: final output (a whole private segment of a sequence in no group),
+    // the sequence's own row for a whole segment of a group member, or a slot row
+    int64_t prow = -1;                            // partial row, or -1
+    int out_row = -1;                             // query row of a final output, or -1
+    if (grp) {
+      const int2 cr = P.cbrec[-1 - cur_q];
+      const int4 gr = P.grp[cr.x];
+      const int mi = cr.y * (16 / G) + n_e / G;
+      if (mi < gr.w) {
+        const int s_e = P.members[gr.z + mi];
+        prow = nseg == 1 ? p.mem_rows0 + (int64_t)(p.share_seqs + s_e) * Hq + qh
+                         : ((int64_t)slot * WPG + wv) * 16 + n_e;
       }
+    } else {
+      const int rr_e = n_e / G;
+      if (rr_e < cur_q) {
+        if (nseg > 1) prow = ((int64_t)slot * WPG + wv) * 16 + n_e;
+        else if (t_off > 0) prow = p.mem_rows0 + (int64_t)s * Hq + qh;   // a group member's own tiles
+        else out_row = row0 + rr_e;
+      }
+    }
+    if (out_row >= 0) {                            // the whole (s, h): final output
+      const float inv = F8 ? p.v_scale / l_tot : 1.f / l_tot;
+      uint16_t* op = p.out + ((size_t)out_row * Hq + qh) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const uint32_t w0 = (uint32_t)f32_to_bf16_rne(oacc[db][0] * inv) | ((uint32_t)f32_to_bf16_rne(oacc[db][1] * inv) << 16);
+        const uint32_t w1 = (uint32_t)f32_to_bf16_rne(oacc[db][2] * inv) | ((uint32_t)f32_to_bf16_rne(oacc[db][3] * inv) << 16);
+        *reinterpret_cast<uint2*>(op + db * 16 + 4 * kg_e) = make_uint2(w0, w1);
+      }
+    } else if (prow >= 0) {                        // a partial for the merge kernel
+      const float vs = F8 ? p.v_scale : 1.f;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        *reinterpret_cast<float4*>(p.ws_o + prow * D + db * 16 + 4 * kg_e) =
+            make_float4(oacc[db][0] * vs, oacc[db][1] * vs, oacc[db][2] * vs, oacc[db][3] * vs);
+      if (kg_e == 0) { p.ws_m[prow] = m_run; p.ws_l[prow] = l_tot; }
     }
   };
 
-  // ---- walk the share: pieces of consecutive (s, head group) segments; this wave takes
-  // the head wv of each group ----
+  // ---- walk the share: pieces of consecutive segments; this wave takes the head wv of each
+  // head group ----
   int pos = x0;
   while (pos < x1) {
-    if (pos >= seg_a + NG * nt) {                // past sequence s: next sequence with decode tiles
-      if (s + 1 >= p.num_seqs) break;            // not reached: pos < total_units
-      next_seq();
+    if (pos >= seg_a + NG * nt) {                // past the current segment (or an empty one)
+      next_seg();
       continue;
     }
     const int hg = (pos - seg_a) / nt;
-    const int a = seg_a + hg * nt;               // first unit of (s, hg)
+    const int a = seg_a + hg * nt;               // first unit of (segment, hg)
     const int tb0 = pos - a;
     const int tb1 = min(x1, a + nt) - a;
     piece(hg * WPG + wv, tb0, tb1, a);
     pos = a + tb1;
   }
+
 }
 
 // Log-sum-exp merge of the pieces of one (decode sequence, query head):
@@ -489,24 +849,39 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(AttnParams p
   const int sub = lane / LPP, dq = lane % LPP;
   // the cell's KV head h, its wave in the decode workgroup and its column g of the group
   const int G = p.Hq / p.Hkv, h = qh / G, g = qh % G, wv_h = h % p.decode_group;
-  // (the piece record is loaded together with the lengths; it is used only for sequences with
-  // decode rows, whose records the decode kernel wrote)
-  const int2 np = p.ws_nparts[(size_t)s * p.Hkv + h];
+  // the records of the sequence's own segment (segment s) and of its sharing group are loaded
+  // together with the lengths; they are used only for sequences with decode rows, whose
+  // records the decode kernel wrote
+  const int2 prv = p.ws_nparts[(size_t)s * p.Hkv + h];
+  const int2 mrec = p.share_seqs > 0 ? p.plan_memrec[s] : make_int2(-1, 0);
   const SeqInfo si = seq_info(p, s);
-  const int nsplit = np.y;
-  // first row of piece j's 16-column block for each wave: piece 0 in slot np.x, piece j > 0 in
-  // slot 0 of the j-th following workgroup
-  auto piece_row = [&](int j) -> size_t {
-    const int slot = j == 0 ? np.x : 2 * (np.x / 2 + j);
-    return (size_t)slot * p.decode_group * 16;
+  if (si.tiles == 0) return;                     // no decode rows (or nothing to attend)
+  const bool member = mrec.x >= 0;               // a member of a prefix-sharing group
+  if (!member && prv.y <= 1) return;             // written directly by the decode kernel
+  const int2 grp = member ? p.ws_nparts[(size_t)mrec.x * p.Hkv + h] : make_int2(0, 0);
+  const int nA = prv.y, nB = member ? grp.y : 0;
+  const int nsplit = nA + nB;
+  // partial row of piece j of decode row rr: the pieces of the sequence's own segment (the
+  // first in slot prv.x, piece j > 0 in slot 0 of the j-th following workgroup; a member's
+  // whole segment in its own row), then those of its group's column block
+  const int64_t slot_rows = (int64_t)p.decode_group * 16;
+  const int64_t stride = 2 * slot_rows;          // from slot 0 of one workgroup to the next
+  const int64_t colA = wv_h * 16 + g, colB = wv_h * 16 + mrec.y + g;
+  const int64_t a0 = (member && nA == 1) ? p.mem_rows0 + (int64_t)s * p.Hq + qh : prv.x * slot_rows + colA;
+  const int64_t a1 = (int64_t)(prv.x / 2 + 1) * stride + colA;
+  const int64_t b0 = nB == 1 ? p.mem_rows0 + (int64_t)(p.share_seqs + s) * p.Hq + qh : grp.x * slot_rows + colB;
+  const int64_t b1 = (int64_t)(grp.x / 2 + 1) * stride + colB;
+  auto piece_row = [&](int j, int rr) -> int64_t {
+    const int64_t r = j < nA ? (j == 0 ? a0 : a1 + (int64_t)(j - 1) * stride)
+                             : (j == nA ? b0 : b1 + (int64_t)(j - nA - 1) * stride);
+    return r + rr * G;                           // decode row rr: column rr G + g (sequences in no group)
   };
   if constexpr (!WIDE) {
     // One pass with a running max, CK wave-wide steps (PPI pieces each) of loads in flight
     // at a time; lanes past the piece count load nothing and are discarded by selection,
     // never by a zero weight.
     constexpr int CK = 4;
-    auto merge_row = [&](int rr, int nsplit, int row0) {
-      const size_t col = (size_t)wv_h * 16 + rr * G + g;   // (wave, column) of this row's head
+    auto merge_row = [&](int rr, int row0) {
       float M = -INFINITY, ls = 0.f;
       float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
       for (int j0 = 0; j0 < nsplit; j0 += CK * PPI) {
@@ -519,7 +894,7 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(AttnParams p
           lj[c] = 0.f;
           o[c] = make_float4(0.f, 0.f, 0.f, 0.f);
           if (j < nsplit) {                      // only the pieces that exist are read
-            const size_t r = piece_row(j) + col;
+            const int64_t r = piece_row(j, rr);
             mj[c] = p.ws_m[r];
             lj[c] = p.ws_l[r];
             o[c] = *reinterpret_cast<const float4*>(p.ws_o + r * D + 4 * dq);
@@ -559,24 +934,21 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(AttnParams p
         *reinterpret_cast<uint2*>(p.out + ((size_t)(row0 + rr) * p.Hq + qh) * D + 4 * dq) = make_uint2(w0, w1);
       }
     };
-    if (si.tiles == 0 || nsplit <= 1) return;    // no decode rows, or written by the decode kernel
-    for (int rr = 0; rr < si.q; ++rr) merge_row(rr, nsplit, si.row0);
+    for (int rr = 0; rr < si.q; ++rr) merge_row(rr, si.row0);
     return;
   }
-  if (si.tiles == 0 || nsplit <= 1) return;      // no decode rows, or written by the decode kernel
   const int w_in = WIDE ? wv : 0;
 
   for (int rr = 0; rr < si.q; ++rr) {
-    const size_t col = (size_t)wv_h * 16 + rr * G + g;
     float M = -INFINITY;                         // every wave of the cell finds the same M
-    for (int j = lane; j < nsplit; j += kWave) M = fmaxf(M, p.ws_m[piece_row(j) + col]);
+    for (int j = lane; j < nsplit; j += kWave) M = fmaxf(M, p.ws_m[piece_row(j, rr)]);
     M = wave_max(M);
 
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float ls = 0.f;
 #pragma unroll 4
     for (int j = w_in * PPI + sub; j < nsplit; j += WPC * PPI) {
-      const size_t r = piece_row(j) + col;
+      const int64_t r = piece_row(j, rr);
       const float f = fast_exp2(p.ws_m[r] - M);   // 0 for a piece that saw no key of this row
       const float4 o = *reinterpret_cast<const float4*>(p.ws_o + r * D + 4 * dq);
       acc.x = fmaf(f, o.x, acc.x); acc.y = fmaf(f, o.y, acc.y);
@@ -612,7 +984,9 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(AttnParams p
 template <int D, int G, int BS, bool F8>
 hipError_t launch_decode_t(const AttnParams& p, hipStream_t stream) {
   const dim3 grid(p.decode_waves / p.decode_group), block(p.decode_group * kWave);
-  const size_t lds = (size_t)p.decode_group * kTile * (D / 8) * 16;   // one bf16 tile per wave
+  // one bf16 tile per wave, then the sharing plan when the call is checked for shared prefixes
+  const size_t lds = (size_t)p.decode_group * kTile * (D / 8) * 16 +
+                     (p.share_seqs > 0 ? (size_t)share_plan_ints(p.share_seqs) * 4 : 0);
   if (p.decode_max_q > 1)
     hipLaunchKernelGGL((decode_kernel<D, G, BS, true, F8>), grid, block, lds, stream, p);
   else
@@ -681,8 +1055,6 @@ hipError_t launch_merge(const AttnParams& p, hipStream_t stream) {
   }
   // the prefill planner rides along as the first workgroup when prefill rows are possible
   q.plan_first = p.max_query_len > p.decode_max_q ? 1 : 0;
-  q.plan_bin_shift = 0;
-  while ((((int64_t)p.max_blocks * p.bs + 63) / 64 >> q.plan_bin_shift) >= kPlanBins) ++q.plan_bin_shift;
   const dim3 grid((unsigned)(q.plan_first + q.merge_blocks + append_blocks));
   const dim3 block(kMergeWaves * kWave);
   if (p.D == 128) {

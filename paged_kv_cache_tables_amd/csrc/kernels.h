@@ -29,16 +29,25 @@ struct AttnParams {
   int decode_max_q;               // sequences with 1 <= q_s <= this are decode rows (q_s x G <= 16)
   int min_share_tiles;            // smallest share of 64-token tiles a decode wave takes
   int max_splits;                 // pieces one (sequence, head) can be cut into (picks the merge form)
-  // Partials of the pieces that do not cover their whole (sequence, head): a decode
-  // workgroup leaves at most two, the first and the last piece of its share (slots 0 and
-  // 1), each with one row of 16 columns per wave.  Partial row of (slot P = 2 workgroup +
-  // slot, wave v, column n): ((P * decode_group + v) * 16 + n).
-  float* ws_o;                    // [decode_waves * 2 * 16, D]  unnormalised partials
-  float* ws_m;                    // [decode_waves * 2 * 16]     partial max (exp2 domain)
-  float* ws_l;                    // [decode_waves * 2 * 16]     partial sum of exponentials
-  int2* ws_nparts;                // [num_seqs, Hkv]  (slot of the first piece, piece count) of each
-                                  // decode (sequence, KV head); later pieces sit in slot 0 of the
+  // Partials.  Rows [0, decode_waves * 32): the pieces that do not cover their whole segment:
+  // a decode workgroup leaves at most two, the first and the last piece of its share (slots 0
+  // and 1), each with one row of 16 columns per wave: row ((2 workgroup + slot) * decode_group
+  // + wave) * 16 + column.  Then, for sequences of a prefix-sharing group, one row per (sequence,
+  // query head) for a whole private segment (row mem_rows0 + s Hq + qh) and one for a whole
+  // group segment (row mem_rows0 + (share_seqs + s) Hq + qh).  Segments: sequence s's own
+  // tiles (segment s), then the sharing groups' column blocks (segments S, S + 1, ...).
+  float* ws_o;                    // [rows, D]  unnormalised partials
+  float* ws_m;                    // [rows]     partial max (exp2 domain)
+  float* ws_l;                    // [rows]     partial sum of exponentials
+  int2* ws_nparts;                // [segments, Hkv]  (slot of the first piece, piece count) of each
+                                  // decode segment and KV head; later pieces sit in slot 0 of the
                                   // following workgroups
+  int64_t mem_rows0;              // first per-(sequence, head) row
+  int share_seqs;                 // sequences checked for shared prefixes: num_seqs, or 0 (no check)
+  int share_hash_slots;           // hash table of the sharing plan: a power of two >= 2 share_seqs
+  int2* plan_memrec;              // [num_seqs] (group segment S + block, first column) of a member
+                                  // of a prefix-sharing group, or (-1, 0); written by the decode
+                                  // kernel's workgroup 0 when share_seqs > 0
   // fused append (paged_attention_append; null k_new otherwise): row i of k_new / v_new is the
   // new token of query row i, stored at slot slots[i].  Decode rows read this step's tokens
   // from k_new / v_new; the merge launch scatters every row into the pools afterwards.
@@ -49,7 +58,7 @@ struct AttnParams {
   uint4* v_pool;
   int merge_blocks;               // merge launch: workgroups that merge (then the append ones)
   int plan_first;                 // merge launch: 1 if its first workgroup plans the prefill items
-  int plan_bin_shift;             // planner: tile counts >> this fit its buckets
+  int plan_bin_shift;             // prefill planner: tile counts >> this fit its buckets
   int2* plan_items;               // prefill work list (sequence, row tile), written by the planner
   int* plan_count;                // number of valid items
   int plan_capacity;              // items the workspace holds
@@ -61,6 +70,9 @@ constexpr int kMaxDecodeGroup = 8;
 
 // Query rows packed into one prefill workgroup (with all G heads of each row).
 constexpr int kPrefillPairs = 128;
+
+// Buckets of the prefill planner's counting sort (planner.h).
+constexpr int kPlanBinsHost = 4096;
 
 hipError_t launch_append(const void* k_new, const void* v_new, const int64_t* slots, int64_t num_tokens,
                          void* k_cache, void* v_cache, int64_t num_slots, int row_chunks,
@@ -74,6 +86,14 @@ hipError_t launch_append_fp8(const void* k_new, const void* v_new, const int64_t
 // chunks per block).
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* src, const int32_t* dst, int n_pairs,
                               int64_t num_blocks, int64_t chunks16, hipStream_t stream);
+
+// Sequences of one call up to which decode rows are checked for shared prefix blocks (the
+// decode workgroups' LDS then bounds it further).
+constexpr int kShareMaxSeqs = 1024;
+
+// Ints of the sharing plan that a decode workgroup keeps in LDS after its tile buffers, for S
+// sequences (S rounded up to a multiple of 4, Sr): 4 + Sr + Sr + 2 Sr + (Sr + 4) + 2 Sr.
+__host__ __device__ constexpr int share_plan_ints(int S) { return 7 * ((S + 3) & ~3) + 8; }
 
 // fp8: the pools hold E4M3 codes instead of bf16.
 bool decode_supported(int D, int G, int bs, bool fp8);

@@ -1,5 +1,5 @@
-// Prefill work list of one attention call, built by one workgroup of the merge launch
-// (which runs after the decode kernel and before the prefill kernel on the same stream).
+// Prefill work list of one attention call, built by one workgroup of the plan launch
+// (which runs before the decode, merge and prefill kernels on the same stream).
 #pragma once
 
 #include "common.h"
@@ -9,7 +9,7 @@ namespace pkv {
 
 // Buckets of the counting sort: item tile counts are shifted right by plan_bin_shift so
 // that the largest fits.
-constexpr int kPlanBins = 4096;
+constexpr int kPlanBins = kPlanBinsHost;
 
 // Lists the prefill work items (sequence, row tile) of one call, longest first.  A
 // sequence with q_s > decode_max_q rows (fewer are computed as decode rows) has

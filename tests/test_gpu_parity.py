@@ -221,6 +221,10 @@ def test_run_to_run_determinism():
 
 
 def test_prefix_sharing_equals_private_copies():
+    """The mixed batch's 100 sharers map one 1024-token prefix; the decode rows among them are
+    attended as sharing groups (the shared tiles read once per block of 16 query columns), so
+    the shared layout and a copy of the prefix per sequence take different paths through the
+    kernels: both must match the oracle, which gives both layouts the same float64 result."""
     wl = W.config3()
     db = DeviceBatch(wl)
     db.step()
@@ -246,7 +250,65 @@ def test_prefix_sharing_equals_private_copies():
     db.k_cache, db.v_cache = k, v
     db.bt = torch.from_numpy(bt.astype(np.int32)).cuda()
     db.attend()
-    assert np.array_equal(to_host_bits(db.out), shared)
+    torch.cuda.synchronize()
+    private = to_host_bits(db.out)
+    k2, v2 = oracle_after_append(wl)
+    ref = oracle.paged_attention(wl.q, k2, v2, wl.block_tables, wl.seq_lens, wl.query_start_loc,
+                                 wl.num_kv_heads, wl.scale)
+    compare(shared, ref, label="mixed-prefix-shared-layout")
+    compare(private, ref, label="mixed-prefix-private-copies")
+
+
+def _share_case(name):
+    """Batches whose decode rows share prefixes in the ways a radix prefix cache produces them."""
+    rng = np.random.default_rng(len(name))
+    if name == "share-two-groups-g4":
+        specs = [(int(x), 1) for x in rng.integers(300, 2000, 40)]
+        specs[3] = (300, 1)
+        own = {21: 128, 22: 80, 23: 16, 24: 48}       # leave the prefix early (the last two: < one tile)
+        share = [(list(range(0, 20)), 256), (list(range(20, 29)), 512, own)]
+        return W.custom(name, specs, 32, 8, 128, 16, seed=1, share=share, row_order=rng.permutation(40))
+    if name == "share-mha-d64-bs8":
+        specs = [(int(x), 1) for x in rng.integers(1100, 1900, 24)]
+        return W.custom(name, specs, 4, 4, 64, 8, seed=2, share=([i for i in range(24) if i % 6], 1024))
+    if name == "share-g16":
+        specs = [(int(x), 1) for x in rng.integers(700, 1500, 8)]
+        return W.custom(name, specs, 16, 1, 128, 16, seed=3, share=([0, 2, 3, 5, 7], 640))
+    if name == "share-g8-bs32-ragged":
+        specs = [(int(x), 1) for x in rng.integers(2100, 3000, 9)]
+        return W.custom(name, specs, 64, 8, 128, 32, seed=4, share=(list(range(7)), 2048))
+    if name == "share-with-prefill-and-multirow":
+        specs = [(int(x), 1) for x in rng.integers(900, 1600, 12)]
+        specs += [(1200, 3), (1500, 2), (1200, 300), (1400, 64), (900, 1)]
+        return W.custom(name, specs, 16, 4, 128, 16, seed=5, share=(list(range(16)), 832),
+                        row_order=rng.permutation(len(specs)))
+    if name == "share-long-prefix":
+        specs = [(20000 + int(x), 1) for x in rng.integers(1, 4000, 10)]
+        return W.custom(name, specs, 32, 8, 128, 16, seed=6, share=(list(range(10)), 20000))
+    if name == "share-one-tile-members":
+        specs = [(65, 1), (66, 1), (64, 1), (200, 1), (129, 1), (65, 1)]
+        return W.custom(name, specs, 8, 2, 128, 16, seed=7, share=([0, 1, 2, 3, 4, 5], 64, {2: 48}))
+    if name == "share-1000-sequences":
+        specs = [(int(x), 1) for x in rng.integers(1025, 1600, 1000)]
+        return W.custom(name, specs, 8, 2, 128, 16, seed=8, share=(list(range(0, 1000, 2)), 1024),
+                        row_order=rng.permutation(1000))
+    if name == "share-beyond-detection":
+        # more sequences than the plan groups: the rows take the private path
+        specs = [(70 + i % 7, 1) for i in range(4100)]
+        return W.custom(name, specs, 8, 2, 128, 16, seed=9, share=(list(range(0, 4100, 3)), 64))
+    raise KeyError(name)
+
+
+SHARE_CASES = ["share-two-groups-g4", "share-mha-d64-bs8", "share-g16", "share-g8-bs32-ragged",
+               "share-with-prefill-and-multirow", "share-long-prefix", "share-one-tile-members",
+               "share-1000-sequences", "share-beyond-detection"]
+
+
+@pytest.mark.parametrize("name", SHARE_CASES)
+def test_shared_prefix_groups(name):
+    wl = _share_case(name)
+    print(f"{name}: {wl.num_seqs} sequences, groups {[len(g) for g in wl.meta['share_groups']]}", flush=True)
+    run_and_check(wl, label=name)
 
 
 def test_caller_workspace_and_stream(gpu):

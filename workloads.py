@@ -201,9 +201,12 @@ def _assemble(name, cfg_id, seed, Hq, Hkv, D, bs, seq_specs, num_blocks=None,
 
     seq_specs: list of (seq_len_after_append, num_new_tokens), indexed by the
                original sequence id.
-    share: None or (set_of_original_seq_ids, prefix_tokens): those sequences'
-           first prefix_tokens/bs table entries point at one common set of
-           blocks that hold one common logical prefix.
+    share: None, (set_of_original_seq_ids, prefix_tokens), or a list of such
+           groups, optionally (ids, prefix_tokens, {id: tokens}): the sequences
+           of a group map one common set of blocks holding one common logical
+           prefix of prefix_tokens tokens -- each its first `tokens` of them
+           (all by default, a whole number of blocks), so that a member can leave
+           the common prefix early and continue with blocks of its own.
     row_order: permutation of original sequence ids giving the batch order.
     """
     n = len(seq_specs)
@@ -212,35 +215,56 @@ def _assemble(name, cfg_id, seed, Hq, Hkv, D, bs, seq_specs, num_blocks=None,
     assert (q0 >= 0).all() and (q0 <= L0).all()
     nblk0 = (L0 + bs - 1) // bs
 
-    sharers = set()
-    share_blocks = 0
-    prefix_tokens = 0
-    if share is not None:
-        sharers, prefix_tokens = share
-        sharers = set(int(s) for s in sharers)
+    if share is None:
+        groups = []
+    elif isinstance(share, list):
+        groups = share
+    else:
+        groups = [share]
+    share_of = {}                 # original id -> (group index, shared tokens)
+    group_blocks = []             # blocks of each group's common prefix
+    group_tokens = []
+    for gi, grp in enumerate(groups):
+        ids, prefix_tokens = grp[0], int(grp[1])
+        own_tokens = grp[2] if len(grp) > 2 else {}
         assert prefix_tokens % bs == 0
-        share_blocks = prefix_tokens // bs
-        for s in sharers:
-            assert L0[s] - q0[s] >= prefix_tokens, "new tokens must land past the shared prefix"
-    unique_blocks = int(nblk0.sum()) - len(sharers) * share_blocks + (share_blocks if sharers else 0)
+        for s in ids:
+            s = int(s)
+            assert s not in share_of, "a sequence belongs to one sharing group"
+            t = int(own_tokens.get(s, prefix_tokens))
+            assert t % bs == 0 and 0 < t <= prefix_tokens
+            assert L0[s] - q0[s] >= t, "new tokens must land past the shared prefix"
+            share_of[s] = (gi, t)
+        group_blocks.append(prefix_tokens // bs if ids else 0)
+        group_tokens.append(prefix_tokens)
+    sharers = set(share_of)
+    share_blocks = group_blocks[0] if groups else 0
+    unique_blocks = int(nblk0.sum()) - sum(t // bs for _, t in share_of.values()) + sum(
+        b for gi, b in enumerate(group_blocks) if any(g == gi for g, _ in share_of.values()))
     if num_blocks is None:
         num_blocks = int(math.ceil(1.1 * unique_blocks))
     assert num_blocks >= unique_blocks
 
     # Block placement: one seeded permutation of the pool; sequences (in
     # original-id order) take consecutive disjoint slices, after the shared
-    # prefix blocks, which come first.
+    # prefix blocks of every group, which come first.
     prng = _rng(seed if placement_seed is None else placement_seed, cfg_id, _S_PLACEMENT)
     perm = prng.permutation(num_blocks).astype(np.int64)
-    shared_ids = perm[:share_blocks] if sharers else perm[:0]
-    cursor = len(shared_ids)
+    cursor = 0
+    shared_ids_of = []
+    for gi, b in enumerate(group_blocks):
+        used = any(g == gi for g, _ in share_of.values())
+        shared_ids_of.append(perm[cursor:cursor + b] if used else perm[:0])
+        cursor += b if used else 0
     max_blocks = int(nblk0.max())
     bt0 = np.full((n, max_blocks), -1, dtype=np.int32)
     for s in range(n):
-        if s in sharers:
-            own = int(nblk0[s]) - share_blocks
-            bt0[s, :share_blocks] = shared_ids
-            bt0[s, share_blocks:share_blocks + own] = perm[cursor:cursor + own]
+        if s in share_of:
+            gi, t = share_of[s]
+            sb = t // bs
+            own = int(nblk0[s]) - sb
+            bt0[s, :sb] = shared_ids_of[gi][:sb]
+            bt0[s, sb:sb + own] = perm[cursor:cursor + own]
             cursor += own
         else:
             bt0[s, :nblk0[s]] = perm[cursor:cursor + nblk0[s]]
@@ -255,18 +279,30 @@ def _assemble(name, cfg_id, seed, Hq, Hkv, D, bs, seq_specs, num_blocks=None,
     qsl[1:] = np.cumsum(qn)
     T = int(qsl[-1])
 
-    prefix_k = prefix_v = None
-    if sharers:
-        r = _rng(seed, cfg_id, _S_KV, 1_000_000)
-        prefix_k = _normal_bf16(r, (prefix_tokens, Hkv, D))
-        prefix_v = _normal_bf16(r, (prefix_tokens, Hkv, D))
-        if outlier_frac:
-            raise NotImplementedError("outliers with a shared prefix are not generated")
+    # the common prefix of each group that has members: its logical K/V and its cached slots
+    prefix_kv = []
+    shared_slots, shared_k, shared_v = [], [], []
+    for gi, ptok in enumerate(group_tokens):
+        if not any(g == gi for g, _ in share_of.values()):
+            prefix_kv.append(None)
+            continue
+        r = _rng(seed, cfg_id, _S_KV, 1_000_000 + gi)
+        pk = _normal_bf16(r, (ptok, Hkv, D))
+        pv = _normal_bf16(r, (ptok, Hkv, D))
+        prefix_kv.append((pk, pv))
+        # slots of the prefix tokens some member maps
+        used_tokens = max(t for g, t in share_of.values() if g == gi)
+        pos = np.arange(used_tokens, dtype=np.int64)
+        shared_slots.append(shared_ids_of[gi][pos // bs] * bs + pos % bs)
+        shared_k.append(pk[:used_tokens])
+        shared_v.append(pv[:used_tokens])
+    if sharers and outlier_frac:
+        raise NotImplementedError("outliers with a shared prefix are not generated")
 
     # Output buffers are allocated once and filled in place by the workers.
-    prior_counts = np.array([int(L[i]) - int(qn[i]) - (prefix_tokens if int(order[i]) in sharers else 0)
+    prior_counts = np.array([int(L[i]) - int(qn[i]) - share_of.get(int(order[i]), (0, 0))[1]
                              for i in range(n)], dtype=np.int64)
-    n_shared = prefix_tokens if sharers else 0
+    n_shared = int(sum(x.size for x in shared_slots))
     coff = np.zeros(n + 1, dtype=np.int64)
     coff[0] = n_shared
     coff[1:] = n_shared + np.cumsum(prior_counts)
@@ -278,21 +314,20 @@ def _assemble(name, cfg_id, seed, Hq, Hkv, D, bs, seq_specs, num_blocks=None,
     cached_slots = np.empty(n_cached, dtype=np.int64)
     cached_k = np.empty((n_cached, Hkv, D), dtype=np.uint16)
     cached_v = np.empty((n_cached, Hkv, D), dtype=np.uint16)
-    if sharers:
-        pos = np.arange(prefix_tokens, dtype=np.int64)
-        cached_slots[:n_shared] = shared_ids[pos // bs] * bs + pos % bs
-        cached_k[:n_shared] = prefix_k
-        cached_v[:n_shared] = prefix_v
+    if n_shared:
+        cached_slots[:n_shared] = np.concatenate(shared_slots)
+        cached_k[:n_shared] = np.concatenate(shared_k)
+        cached_v[:n_shared] = np.concatenate(shared_v)
 
     def one(i):
         s_orig = int(order[i])
         Ls, qs = int(L[i]), int(qn[i])
         prior = Ls - qs
-        shared = s_orig in sharers
         # Logical K/V for positions 0..Ls-1, keyed by the original sequence id
-        # so that placement, block size and row order leave the data unchanged.
+        # so that placement, block size and row order leave the data unchanged
+        # (positions before `start` are the group's common prefix).
         r = _rng(seed, cfg_id, _S_KV, s_orig)
-        start = prefix_tokens if shared else 0
+        start = share_of.get(s_orig, (0, 0))[1]
         kl = _normal_bf16(r, (Ls - start, Hkv, D))
         vl = _normal_bf16(r, (Ls - start, Hkv, D))
         if outlier_frac:
@@ -321,9 +356,11 @@ def _assemble(name, cfg_id, seed, Hq, Hkv, D, bs, seq_specs, num_blocks=None,
     _par_map(one, range(n))
 
     scale = float(np.float32(1.0) / np.sqrt(np.float32(D)))
-    sharers_new = sorted(int(np.nonzero(order == s)[0][0]) for s in sharers)
+    pos_of = {int(s): int(i) for i, s in enumerate(order)}
+    sharers_new = sorted(pos_of[s] for s in sharers)
+    share_groups = [sorted(pos_of[s] for s, (g, _) in share_of.items() if g == gi) for gi in range(len(groups))]
     meta = dict(config=cfg_id, seed=seed, unique_blocks=unique_blocks,
-                sharers=sharers_new, share_blocks=share_blocks)
+                sharers=sharers_new, share_blocks=share_blocks, share_groups=share_groups)
     if extra_meta:
         meta.update(extra_meta)
     return Workload(name=name, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=bs,
