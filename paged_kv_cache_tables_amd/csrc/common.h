@@ -49,6 +49,14 @@ __device__ __forceinline__ void e4m3x16_to_bf16(uint4 v, uint4& lo, uint4& hi) {
 #undef PKV_CVT2
 }
 
+// Read of an int that is not written during the kernel, at a wave-uniform index, through
+// the scalar data cache (s_load_dword): its wait is on the scalar counter, so it never waits
+// for the wave's vector loads in flight.  Reads only; nothing is written this way.
+typedef const __attribute__((address_space(4))) int const_int_as4;
+__device__ __forceinline__ int load_uniform_int(const int* base, int idx) {
+  return ((const_int_as4*)base)[idx];
+}
+
 // 2^x with the hardware instruction (results below 2^-126 flush to zero, which for
 // softmax weights relative to a maximum weight of 1 is far below fp32 resolution).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -554,12 +554,16 @@ void decode_kernel(AttnParams p) {
     for (int db = 0; db < DB; ++db) oacc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_part = 0.f;
 
-    // Block-table entries of a tile (wave-uniform scalar loads).  Entries past the end,
-    // or outside the pool, become block 0: a safe address whose rows the masks ignore.
+    // Block-table entries of a tile (wave-uniform loads).  Entries past the end, or outside
+    // the pool, become block 0: a safe address whose rows the masks ignore.  For 8-bit pools
+    // they come through the scalar cache, so the wait for them is not a wait for the tile
+    // loads in flight (measured: Llama-3-8B batch 74 -> 68 us per call; for bf16 pools the
+    // vector form measured 2-3% faster on the 70B and long-context batches).
     auto load_bts = [&](int t0, int* dst) {
 #pragma unroll
       for (int j = 0; j < NBT; ++j) {
-        const int b = (t0 + j * BS < t_end) ? bt_row[uniform((t0 + j * BS) / BS)] : 0;
+        const int e = uniform((t0 + j * BS) / BS);
+        const int b = (t0 + j * BS < t_end) ? (F8 ? load_uniform_int(bt_row, e) : bt_row[e]) : 0;
         dst[j] = (unsigned)b < (unsigned)nblocks ? b : 0;
       }
     };
