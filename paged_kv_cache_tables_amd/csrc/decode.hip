@@ -373,14 +373,18 @@ void decode_kernel(AttnParams p) {
   // the host). ----
   const int S = p.num_seqs;
   const int c_per = (S + kWave - 1) / kWave;
-  // sharing check: the candidates' first blocks in a hash table (share_hash_slots >= 2 S
-  // entries, a power of two) at the start of this wave's tile buffer
+  // sharing check, by all waves of the workgroup together: the candidates' first blocks in one
+  // hash table (share_hash_slots >= 2 S entries, a power of two) at the start of wave 0's tile
+  // buffer, each wave inserting every WPG-th element of the lanes' chunks; a wave that finds a
+  // repeated block sets an LDS flag
   const bool detect = p.share_seqs > 0;
-  int* whash = reinterpret_cast<int*>(&tile[0][0]);
+  __shared__ int share_flag;
+  int* whash = reinterpret_cast<int*>(lds_tiles);
   const int HS = p.share_hash_slots;
   if (detect) {
-    for (int i = lane; i < HS / 4; i += kWave) reinterpret_cast<uint4*>(whash)[i] = make_uint4(~0u, ~0u, ~0u, ~0u);
-    wave_lds_sync();
+    for (int i = threadIdx.x; i < HS / 4; i += (int)blockDim.x) reinterpret_cast<uint4*>(whash)[i] = make_uint4(~0u, ~0u, ~0u, ~0u);
+    if (threadIdx.x == 0) share_flag = 0;
+    __syncthreads();                             // the table is clear
   }
   const int nblocks_i = p.num_blocks > 0x7fffffff ? 0x7fffffff : (int)p.num_blocks;
   int my_tiles = 0;
@@ -396,13 +400,13 @@ void decode_kernel(AttnParams p) {
       const int s = lane * c_per + i0 + k;
       const bool ok = i0 + k < c_per && s < S;
       si[k] = ok ? seq_info(p, s) : SeqInfo{0, 0, 0, 0};
-      b0[k] = (ok && detect) ? p.block_tables[(size_t)s * p.max_blocks] : -1;
+      b0[k] = (ok && detect && (i0 + k) % WPG == wv) ? p.block_tables[(size_t)s * p.max_blocks] : -1;
     }
     if (i0 == 0) first = si[0];
 #pragma unroll
     for (int k = 0; k < kSeqBatch; ++k) {
       my_tiles += si[k].tiles;
-      if (detect && si[k].q == 1 && si[k].tiles >= 2 && (unsigned)b0[k] < (unsigned)nblocks_i) {
+      if (detect && si[k].q == 1 && si[k].tiles >= 2 && (unsigned)b0[k] < (unsigned)nblocks_i) {   // (b0 only for this wave's elements)
         unsigned h = ((unsigned)b0[k] * 2654435761u) & (unsigned)(HS - 1);
         for (int probe = 0; probe < HS; ++probe) {   // at most S keys in HS >= 2 S slots
           const int prev = atomicCAS(&whash[h], -1, b0[k]);
@@ -413,13 +417,17 @@ void decode_kernel(AttnParams p) {
       }
     }
   }
-  // every wave of the workgroup finds the same answer (the same keys)
-  const bool sharing = detect && __builtin_amdgcn_ballot_w64(dup) != 0;
+  bool sharing = false;
+  if (detect) {
+    const bool any_dup = __builtin_amdgcn_ballot_w64(dup) != 0;
+    if (any_dup && lane == 0) share_flag = 1;
+    __syncthreads();                             // every insert and flag write is done
+    sharing = uniform(share_flag) != 0;
+  }
   if (detect && !sharing && w == 0)              // no group: the merge kernel sees no member
     for (int i = threadIdx.x; i < S; i += blockDim.x) p.plan_memrec[i] = make_int2(-1, 0);
   const SharePlan P(reinterpret_cast<int*>(lds_tiles + (size_t)WPG * kTile * CH), S);
   if (sharing) {
-    __syncthreads();                             // every wave is done with its own table
     build_share_plan(p, reinterpret_cast<int*>(lds_tiles), P, NG, G);
     for (int i = 0; i < c_per; ++i) {
       const int s = lane * c_per + i;
