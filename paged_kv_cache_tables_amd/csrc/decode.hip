@@ -377,11 +377,16 @@ void decode_kernel(AttnParams p) {
   // hash table (share_hash_slots >= 2 S entries, a power of two) at the start of wave 0's tile
   // buffer, each wave inserting every WPG-th element of the lanes' chunks; a wave that finds a
   // repeated block sets an LDS flag
+  // With at most 64 sequences (one per lane) each wave instead sorts the lanes' first blocks
+  // and compares neighbours: no table, no barrier.
   const bool detect = p.share_seqs > 0;
+  const bool wave_check = detect && c_per == 1;
+  const bool table_check = detect && !wave_check;
   __shared__ int share_flag;
   int* whash = reinterpret_cast<int*>(lds_tiles);
   const int HS = p.share_hash_slots;
-  if (detect) {
+  int wkey = -1 - lane;                          // the lane's candidate key (a distinct negative one if none)
+  if (table_check) {
     for (int i = threadIdx.x; i < HS / 4; i += (int)blockDim.x) reinterpret_cast<uint4*>(whash)[i] = make_uint4(~0u, ~0u, ~0u, ~0u);
     if (threadIdx.x == 0) share_flag = 0;
     __syncthreads();                             // the table is clear
@@ -400,13 +405,15 @@ void decode_kernel(AttnParams p) {
       const int s = lane * c_per + i0 + k;
       const bool ok = i0 + k < c_per && s < S;
       si[k] = ok ? seq_info(p, s) : SeqInfo{0, 0, 0, 0};
-      b0[k] = (ok && detect && (i0 + k) % WPG == wv) ? p.block_tables[(size_t)s * p.max_blocks] : -1;
+      b0[k] = (ok && (wave_check || (table_check && (i0 + k) % WPG == wv))) ? p.block_tables[(size_t)s * p.max_blocks] : -1;
     }
     if (i0 == 0) first = si[0];
 #pragma unroll
     for (int k = 0; k < kSeqBatch; ++k) {
       my_tiles += si[k].tiles;
-      if (detect && si[k].q == 1 && si[k].tiles >= 2 && (unsigned)b0[k] < (unsigned)nblocks_i) {   // (b0 only for this wave's elements)
+      const bool cand = si[k].q == 1 && si[k].tiles >= 2 && (unsigned)b0[k] < (unsigned)nblocks_i;
+      if (wave_check && k == 0 && cand) wkey = b0[k];
+      if (table_check && cand) {                 // (b0 only for this wave's elements)
         unsigned h = ((unsigned)b0[k] * 2654435761u) & (unsigned)(HS - 1);
         for (int probe = 0; probe < HS; ++probe) {   // at most S keys in HS >= 2 S slots
           const int prev = atomicCAS(&whash[h], -1, b0[k]);
@@ -418,7 +425,19 @@ void decode_kernel(AttnParams p) {
     }
   }
   bool sharing = false;
-  if (detect) {
+  if (wave_check) {
+    // bitonic sort of the 64 keys across the lanes (ascending), then equal neighbours
+#pragma unroll
+    for (int kk = 2; kk <= kWave; kk <<= 1)
+#pragma unroll
+      for (int j = kk >> 1; j > 0; j >>= 1) {
+        const int o = __shfl_xor(wkey, j, kWave);
+        const bool keep_min = ((lane & j) == 0) == ((lane & kk) == 0);
+        wkey = keep_min ? min(wkey, o) : max(wkey, o);
+      }
+    const int prev = __shfl_up(wkey, 1, kWave);
+    sharing = __builtin_amdgcn_ballot_w64(lane > 0 && wkey >= 0 && prev == wkey) != 0;
+  } else if (table_check) {
     const bool any_dup = __builtin_amdgcn_ballot_w64(dup) != 0;
     if (any_dup && lane == 0) share_flag = 1;
     __syncthreads();                             // every insert and flag write is done
