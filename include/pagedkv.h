@@ -140,6 +140,14 @@ PKV_API int kv_append(const void* k_new, const void* v_new, const int64_t* slot_
  * accumulate in fp32.  out is rounded to bf16
  * (nearest-even).  Positions >= L and unreferenced blocks are never read into
  * the result (they may hold any bits, NaN included).
+ * Shared prefixes ([TGI] "Under the Hood: PagedAttention", prefix sharing):
+ * when decode sequences with one row each have block tables that begin with
+ * the same physical blocks, the library finds them from the tables (batches
+ * of up to 1024 sequences at head_dim 128 with 8 or more KV heads; fewer
+ * with fewer KV heads or at head_dim 64) and reads the common whole 64-token
+ * tiles once per 16 query
+ * columns instead of once per sequence.  The result is the same attention;
+ * only the order in which partial sums are combined differs.
  *
  *   out            device, bf16 [num_q_tokens, num_q_heads, head_dim], written.
  *   q              device, bf16 [num_q_tokens, num_q_heads, head_dim].
@@ -165,10 +173,10 @@ PKV_API int kv_append(const void* k_new, const void* v_new, const int64_t* slot_
  *                  caller passes (PKV_EWORKSPACE if smaller than required).
  *                  The size depends only on num_seqs, num_q_heads,
  *                  num_kv_heads, head_dim, max_blocks_per_seq, block_size
- *                  and max_query_len (through min(max_query_len,
- *                  16 / (num_q_heads / num_kv_heads))).  The buffer needs no
- *                  initialisation and must not be shared by calls that can
- *                  run concurrently.
+ *                  and the current device (its compute-unit count sizes the
+ *                  decode partials), not on max_query_len.  The buffer needs
+ *                  no initialisation and must not be shared by calls that
+ *                  can run concurrently.
  *   stream         hipStream_t.
  *
  * Contract: 1 <= q_s <= L for every sequence with rows (q_s = 0 is allowed

@@ -20,9 +20,9 @@
 // accumulation and the vector ALUs are left with the softmax.
 //
 // Layout (gfx950, v_mfma_f32_16x16x32_bf16):
-//   * Partition (built by the plan kernel, plan.hip): the decode rows' work is
-//     cut into units (segment, group of KV heads, 64-token tile), in that
-//     order.  A segment is a sequence's own tiles, or the tiles a group of
+//   * Partition (found by every wave from the lengths, with a wave scan; no
+//     host work): the decode rows' work is cut into units (segment, group of
+//     KV heads, 64-token tile), in that order.  A segment is a sequence's own tiles, or the tiles a group of
 //     sequences maps to the same physical blocks (a shared prefix) for a block
 //     of 16 query columns of its members.  The grid has one wave per resident
 //     wave slot of the device; a workgroup holds one wave per KV head of a
@@ -75,9 +75,10 @@ typedef __attribute__((address_space(3))) short4v lds_short4;
 // prefix ("Under the Hood: PagedAttention", prefix sharing: one cached copy, several block
 // tables pointing at it -- Text Generation Inference page; the radix prefix cache of the
 // text-generation-inference v3 walkthrough builds such tables).  Attending that prefix once
-// per sequence re-reads the same K/V.  Every decode wave first checks, in its own LDS tile
-// buffer, whether two decode sequences (one query row each) start with the same block.  If
-// none do, the partition below is the plain per-sequence one.  If some do, every workgroup
+// per sequence re-reads the same K/V.  Every decode workgroup first checks whether two decode
+// sequences (one query row each) start with the same block: up to 64 sequences, each wave
+// sorts the lanes' first blocks; beyond that, its waves fill one hash table in LDS together.
+// If none do, the partition below is the plain per-sequence one.  If some do, every workgroup
 // builds the same sharing plan in LDS (the tile buffers as scratch, a small region after
 // them for the result): the sequences with a common first block form a group under the
 // first of them (the leader); each member's block table is compared with the leader's,
