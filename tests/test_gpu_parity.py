@@ -289,11 +289,13 @@ def _share_case(name):
         specs = [(65, 1), (66, 1), (64, 1), (200, 1), (129, 1), (65, 1)]
         return W.custom(name, specs, 8, 2, 128, 16, seed=7, share=([0, 1, 2, 3, 4, 5], 64, {2: 48}))
     if name == "share-1000-sequences":
+        # 8 KV heads per decode workgroup: detection runs up to 1024 sequences (16 per lane)
         specs = [(int(x), 1) for x in rng.integers(1025, 1600, 1000)]
-        return W.custom(name, specs, 8, 2, 128, 16, seed=8, share=(list(range(0, 1000, 2)), 1024),
+        return W.custom(name, specs, 16, 8, 128, 16, seed=8, share=(list(range(0, 1000, 2)), 1024),
                         row_order=rng.permutation(1000))
     if name == "share-beyond-detection":
-        # more sequences than the plan groups: the rows take the private path
+        # more sequences than detection covers (256 with 2 KV heads per workgroup): the rows
+        # take the private path
         specs = [(70 + i % 7, 1) for i in range(4100)]
         return W.custom(name, specs, 8, 2, 128, 16, seed=9, share=(list(range(0, 4100, 3)), 64))
     raise KeyError(name)
