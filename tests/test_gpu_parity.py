@@ -257,6 +257,9 @@ def test_prefix_sharing_equals_private_copies():
                                  wl.num_kv_heads, wl.scale)
     compare(shared, ref, label="mixed-prefix-shared-layout")
     compare(private, ref, label="mixed-prefix-private-copies")
+    # only block ids differ: without the sharing groups both layouts would take the same path
+    # and agree bit for bit
+    assert not np.array_equal(shared, private), "the shared layout did not take the group path"
 
 
 def _share_case(name):
@@ -301,6 +304,41 @@ def _share_case(name):
     raise KeyError(name)
 
 
+def private_copies(db, wl):
+    """Give every sequence its own copy of each block it shares with another (the pools are
+    extended; the first sequence to reference a block keeps it).  Only block ids change, so
+    the attention is the same; without sharing groups the kernels take the same path for
+    both layouts and agree bit for bit."""
+    import torch
+    bt = wl.block_tables.copy()
+    nblk = (wl.seq_lens.astype(np.int64) + wl.block_size - 1) // wl.block_size
+    refs = {}
+    for s in range(wl.num_seqs):
+        for j in range(int(nblk[s])):
+            refs[int(bt[s, j])] = refs.get(int(bt[s, j]), 0) + 1
+    seen, moves, nxt = set(), [], wl.num_blocks
+    for s in range(wl.num_seqs):
+        for j in range(int(nblk[s])):
+            b = int(bt[s, j])
+            if refs[b] > 1 and b in seen:
+                moves.append((nxt, b))
+                bt[s, j] = nxt
+                nxt += 1
+            seen.add(b)
+    k = torch.empty((nxt,) + tuple(db.k_cache.shape[1:]), dtype=db.k_cache.dtype, device=db.k_cache.device)
+    v = torch.empty_like(k)
+    k[:wl.num_blocks] = db.k_cache
+    v[:wl.num_blocks] = db.v_cache
+    if moves:
+        dst = torch.tensor([m[0] for m in moves], device=k.device)
+        src = torch.tensor([m[1] for m in moves], device=k.device)
+        k[dst] = db.k_cache[src]
+        v[dst] = db.v_cache[src]
+    db.k_cache, db.v_cache = k, v
+    db.bt = torch.from_numpy(bt.astype(np.int32)).to(k.device)
+    return len(moves)
+
+
 SHARE_CASES = ["share-two-groups-g4", "share-mha-d64-bs8", "share-g16", "share-g8-bs32-ragged",
                "share-with-prefill-and-multirow", "share-long-prefix", "share-one-tile-members",
                "share-1000-sequences", "share-beyond-detection"]
@@ -308,9 +346,26 @@ SHARE_CASES = ["share-two-groups-g4", "share-mha-d64-bs8", "share-g16", "share-g
 
 @pytest.mark.parametrize("name", SHARE_CASES)
 def test_shared_prefix_groups(name):
+    """Both layouts (shared blocks, and a private copy per sequence) against the oracle; the
+    shared layout must take the group path (its output differs in rounding from the private
+    layout's) except beyond the detection limit, where both take the same path."""
     wl = _share_case(name)
     print(f"{name}: {wl.num_seqs} sequences, groups {[len(g) for g in wl.meta['share_groups']]}", flush=True)
-    run_and_check(wl, label=name)
+    db, shared, _ = run_and_check(wl, label=name)
+    moved = private_copies(db, wl)
+    db.attend()
+    import torch
+    torch.cuda.synchronize()
+    private = to_host_bits(db.out)
+    k2, v2 = oracle_after_append(wl)
+    ref = oracle.paged_attention(wl.q, k2, v2, wl.block_tables, wl.seq_lens, wl.query_start_loc,
+                                 wl.num_kv_heads, wl.scale)
+    compare(private, ref, label=name + "-private-copies")
+    assert moved > 0
+    if name == "share-beyond-detection":
+        assert np.array_equal(shared, private)
+    else:
+        assert not np.array_equal(shared, private), "the shared layout did not take the group path"
 
 
 def test_caller_workspace_and_stream(gpu):
