@@ -791,8 +791,8 @@ void decode_kernel(AttnParams p) {
       uint16_t* op = p.out + ((size_t)out_row * Hq + qh) * D;
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const uint32_t w0 = (uint32_t)f32_to_bf16_rne(oacc[db][0] * inv) | ((uint32_t)f32_to_bf16_rne(oacc[db][1] * inv) << 16);
-        const uint32_t w1 = (uint32_t)f32_to_bf16_rne(oacc[db][2] * inv) | ((uint32_t)f32_to_bf16_rne(oacc[db][3] * inv) << 16);
+        const uint32_t w0 = pack_bf16x2(oacc[db][0] * inv, oacc[db][1] * inv);
+        const uint32_t w1 = pack_bf16x2(oacc[db][2] * inv, oacc[db][3] * inv);
         *reinterpret_cast<uint2*>(op + db * 16 + 4 * kg_e) = make_uint2(w0, w1);
       }
     } else if (prow >= 0) {                        // a partial for the merge kernel
@@ -961,8 +961,8 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(AttnParams p
       }
       if (sub == 0) {
         const float inv = 1.f / ls;
-        const uint32_t w0 = (uint32_t)f32_to_bf16_rne(acc.x * inv) | ((uint32_t)f32_to_bf16_rne(acc.y * inv) << 16);
-        const uint32_t w1 = (uint32_t)f32_to_bf16_rne(acc.z * inv) | ((uint32_t)f32_to_bf16_rne(acc.w * inv) << 16);
+        const uint32_t w0 = pack_bf16x2(acc.x * inv, acc.y * inv);
+        const uint32_t w1 = pack_bf16x2(acc.z * inv, acc.w * inv);
         *reinterpret_cast<uint2*>(p.out + ((size_t)(row0 + rr) * p.Hq + qh) * D + 4 * dq) = make_uint2(w0, w1);
       }
     };
@@ -1006,8 +1006,8 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void merge_kernel(AttnParams p
     }
     if (sub == 0 && w_in == 0) {
       const float inv = 1.f / ls;
-      const uint32_t w0 = (uint32_t)f32_to_bf16_rne(acc.x * inv) | ((uint32_t)f32_to_bf16_rne(acc.y * inv) << 16);
-      const uint32_t w1 = (uint32_t)f32_to_bf16_rne(acc.z * inv) | ((uint32_t)f32_to_bf16_rne(acc.w * inv) << 16);
+      const uint32_t w0 = pack_bf16x2(acc.x * inv, acc.y * inv);
+      const uint32_t w1 = pack_bf16x2(acc.z * inv, acc.w * inv);
       *reinterpret_cast<uint2*>(p.out + ((size_t)(si.row0 + rr) * p.Hq + qh) * D + 4 * dq) = make_uint2(w0, w1);
     }
   }

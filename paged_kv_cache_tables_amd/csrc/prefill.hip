@@ -455,10 +455,8 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int d = dt * 32 + 8 * q4 + 4 * kg;
-      const uint32_t w0 = (uint32_t)f32_to_bf16_rne(oacc[dt][q4 * 4 + 0] * inv) |
-                          ((uint32_t)f32_to_bf16_rne(oacc[dt][q4 * 4 + 1] * inv) << 16);
-      const uint32_t w1 = (uint32_t)f32_to_bf16_rne(oacc[dt][q4 * 4 + 2] * inv) |
-                          ((uint32_t)f32_to_bf16_rne(oacc[dt][q4 * 4 + 3] * inv) << 16);
+      const uint32_t w0 = pack_bf16x2(oacc[dt][q4 * 4 + 0] * inv, oacc[dt][q4 * 4 + 1] * inv);
+      const uint32_t w1 = pack_bf16x2(oacc[dt][q4 * 4 + 2] * inv, oacc[dt][q4 * 4 + 3] * inv);
       *reinterpret_cast<uint2*>(op + d) = make_uint2(w0, w1);
     }
 }
