@@ -136,8 +136,10 @@ PKV_API int kv_append(const void* k_new, const void* v_new, const int64_t* slot_
  * Rows of sequences with q_s <= 16 / (num_q_heads / num_kv_heads) -- decode
  * rows and short chunks such as speculative-decoding verification -- share one
  * K/V read per sequence and KV head through split-K with a log-sum-exp merge;
- * longer chunks (chunked prefill) use tiled bf16 matrix-core products.  Both
- * accumulate in fp32.  out is rounded to bf16
+ * longer chunks (chunked prefill) use tiled bf16 matrix-core products, and
+ * when a call has too few chunk tiles to occupy the device (a chunk over a
+ * long prefix) their long key ranges are cut into pieces whose partial
+ * results are merged the same way.  Both accumulate in fp32.  out is rounded to bf16
  * (nearest-even).  Positions >= L and unreferenced blocks are never read into
  * the result (they may hold any bits, NaN included).
  * Shared prefixes ([TGI] "Under the Hood: PagedAttention", prefix sharing):
@@ -245,9 +247,10 @@ PKV_API int paged_attention_append(void* out, const void* q, const void* k_new, 
  *
  * Returns what paged_attention_append returns, or PKV_ESCRATCH (nothing
  * enqueued) when the shape needs more scratch than PKV_NOALLOC_SCRATCH_BYTES
- * (paged_attention's workspace query gives the size a shape needs; e.g. 64
- * sequences of up to 4096 tokens with 32 query heads of dimension 128 need
- * about 10 MB, 4 sequences of 131072 tokens with 64 query heads about 34 MB).
+ * (paged_attention's workspace query gives the size a shape needs; on a
+ * 256-CU device, 64 sequences of up to 4096 tokens with 32 query heads of
+ * dimension 128 need about 36 MB, 4 sequences of 131072 tokens with 64 query
+ * heads about 35 MB: most of it is the decode partials, sized by the CU count).
  */
 #define PKV_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 PKV_API int paged_attention_append_noalloc(void* out, const void* q, const void* k_new, const void* v_new,

@@ -24,6 +24,8 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 struct WsLayout {
   int64_t max_splits;
   int64_t plan_capacity;
+  int64_t piece_cap;
+  size_t ctr_off;
   int64_t share_seqs, mem_rows0;
   size_t o_off, m_off, l_off, nparts_off, memrec_off, count_off, items_off, total;
 };
@@ -82,7 +84,8 @@ WsLayout workspace_layout(int num_seqs, int Hq, int Hkv, int D, int max_blocks, 
   const int64_t max_tokens = (int64_t)max_blocks * bs;
   w.max_splits = (max_tokens + kMinShareTokens - 1) / kMinShareTokens + 1;
   const int rows = pkv::kPrefillPairs / (Hq / Hkv);
-  w.plan_capacity = (int64_t)num_seqs * ((max_tokens + rows - 1) / rows);
+  w.piece_cap = (int64_t)decode_waves * 2 * 16 / pkv::kPrefillPairs;   // split prefill items reuse the decode partial rows
+  w.plan_capacity = (int64_t)num_seqs * ((max_tokens + rows - 1) / rows) + w.piece_cap;
   w.share_seqs = num_seqs <= share_cap(D, group) ? num_seqs : 0;
   w.mem_rows0 = (int64_t)decode_waves * 2 * 16;
   const size_t prows = (size_t)w.mem_rows0 + 2 * (size_t)w.share_seqs * Hq;
@@ -93,8 +96,9 @@ WsLayout workspace_layout(int num_seqs, int Hq, int Hkv, int D, int max_blocks, 
   w.nparts_off = w.l_off + round_up(prows * sizeof(float), 256);
   w.memrec_off = w.nparts_off + round_up(nseg * Hkv * 2 * sizeof(int), 256);
   w.count_off = w.memrec_off + round_up((size_t)w.share_seqs * 2 * sizeof(int), 256);
-  w.items_off = w.count_off + 256;
-  w.total = w.items_off + round_up((size_t)w.plan_capacity * 8, 256);
+  w.ctr_off = w.count_off + 256;
+  w.items_off = w.ctr_off + round_up((size_t)w.piece_cap * sizeof(int), 256);
+  w.total = w.items_off + round_up((size_t)w.plan_capacity * 16, 256);
   return w;
 }
 
@@ -306,13 +310,19 @@ int attention_impl(void* out, const void* q, const void* k_cache, const void* v_
   while ((((int64_t)max_blocks_per_seq * block_size + 63) / 64 >> p.plan_bin_shift) >= pkv::kPlanBinsHost)
     ++p.plan_bin_shift;
   p.plan_count = (int*)(wsb + ws.count_off);
-  p.plan_items = (int2*)(wsb + ws.items_off);
+  p.plan_items = (int4*)(wsb + ws.items_off);
+  p.plan_split_ctr = (int*)(wsb + ws.ctr_off);
+  p.prefill_piece_cap = (int)ws.piece_cap;
+  // prefill workgroups resident at once: two per compute unit (their registers and LDS)
+  p.prefill_slots = std::max(1, decode_waves / kDecodeWavesPerCU) * 2;
   p.plan_capacity = (int)ws.plan_capacity;
   {
     // bound on the prefill items of this call: sum over sequences with q_s > 1 of
     // ceil(q_s / rows) <= num_q_tokens / rows + (number of such sequences)
     const int rows = pkv::kPrefillPairs / G;
-    const int64_t bound = (num_q_tokens + rows - 1) / rows + std::min<int64_t>(num_seqs, num_q_tokens / 2);
+    // plus the extra pieces of split items (at most the partial slots of one head)
+    const int64_t bound = (num_q_tokens + rows - 1) / rows + std::min<int64_t>(num_seqs, num_q_tokens / 2) +
+                          ws.piece_cap / num_kv_heads;
     p.plan_stride = (int)std::min<int64_t>(bound, ws.plan_capacity);
   }
 

@@ -59,10 +59,14 @@ struct AttnParams {
   int merge_blocks;               // merge launch: workgroups that merge (then the append ones)
   int plan_first;                 // merge launch: 1 if its first workgroup plans the prefill items
   int plan_bin_shift;             // prefill planner: tile counts >> this fit its buckets
-  int2* plan_items;               // prefill work list (sequence, row tile), written by the planner
-  int* plan_count;                // number of valid items
-  int plan_capacity;              // items the workspace holds
-  int plan_stride;                // host bound on the items of this call (grid = Hkv * stride)
+  int4* plan_items;               // prefill work list, written by the planner: (sequence, row tile,
+                                  // piece | pieces << 16, first partial slot of a split item)
+  int* plan_count;                // number of valid entries
+  int plan_capacity;              // entries the workspace holds
+  int plan_stride;                // host bound on the entries of this call (grid = Hkv * stride)
+  int prefill_slots;              // prefill workgroups resident at once (two per compute unit)
+  int prefill_piece_cap;          // partial slots of split items, all KV heads (rows of ws_o / 128)
+  int* plan_split_ctr;            // [prefill_piece_cap] finished pieces per (split item, KV head)
 };
 
 // Most KV heads (waves) one decode workgroup takes together.
@@ -73,6 +77,11 @@ constexpr int kPrefillPairs = 128;
 
 // Buckets of the prefill planner's counting sort (planner.h).
 constexpr int kPlanBinsHost = 4096;
+
+// Prefill items of more than kSplitMinTiles key tiles (64 keys each) may be cut into at most
+// kMaxPieces pieces of consecutive tiles when the call has too few items to fill the device.
+constexpr int kSplitMinTiles = 64;
+constexpr int kMaxPieces = 32;
 
 hipError_t launch_append(const void* k_new, const void* v_new, const int64_t* slots, int64_t num_tokens,
                          void* k_cache, void* v_cache, int64_t num_slots, int row_chunks,

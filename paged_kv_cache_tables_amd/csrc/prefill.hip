@@ -80,6 +80,19 @@ __device__ __forceinline__ void wait_lds() {
   __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (N << 8) | (3 << 14));
 }
 
+// Two floats at an 8-byte aligned address, stored and loaded at agent scope: the store is
+// written through to the level where all XCDs of the device see it, the load reads from
+// there (never a stale copy in this XCD's L2).
+__device__ __forceinline__ void store_coherent2(float* p, float a, float b) {
+  const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_coherent2(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+
 // Workgroup barrier for LDS hand-over: no memory operation moves across it in the
 // compiler, and unlike __syncthreads() it does not wait for this wave's outstanding
 // global loads (the tiles in flight).  LDS reads before it have been consumed by then.
@@ -127,8 +140,11 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
   // longest-first order; items past the planner's count do nothing
   const int h = (int)(blockIdx.x % p.Hkv), item = (int)(blockIdx.x / p.Hkv);
   if (item >= *p.plan_count || item >= p.plan_capacity) return;
-  const int2 it = p.plan_items[item];
+  const int4 it = p.plan_items[item];
   const int s = it.x, mt = it.y;
+  const int piece = it.z & 0xffff, npieces = it.z >> 16;   // keys of piece `piece` of npieces
+  const int slot0 = it.w;                        // first partial slot of a split item
+  if (npieces < 1 || piece >= npieces) return;
   const int row0 = p.qsl[s];
   const int qn = p.qsl[s + 1] - row0;
   if (qn <= p.decode_max_q) return;              // decode rows are handled elsewhere
@@ -394,14 +410,19 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
   // ---- pipeline over tiles: tile t in buffer t % kBuf, the next kBuf - 1 tiles in flight ----
   // Per thread, a tile is 2 NLD loads (K then V) issued in tile order, so "tile t has
   // landed" is "at most the loads of the tiles issued after it are outstanding".
-  const int ntiles = (key_end + kKT - 1) / kKT;
+  // A piece covers the item's key tiles [kt0, kt1): tile t of the loop is key tile kt0 + t.
+  const int item_tiles = (key_end + kKT - 1) / kKT;
+  // (item_tiles < 2^25 and npieces <= 32: the products fit 32 bits)
+  const int kt0 = npieces == 1 ? 0 : (int)((uint32_t)(piece * item_tiles) / (uint32_t)npieces);
+  const int ntiles = npieces == 1 ? item_tiles : (int)((uint32_t)((piece + 1) * item_tiles) / (uint32_t)npieces) - kt0;
+  const int kb0 = kt0 * kKT;
   if constexpr (!F8) {
-    int btv = fetch_bt(0);
-    issue(IntC<0>(), 0, btv);
-    if (ntiles > 1) btv = fetch_bt(kKT);
+    int btv = fetch_bt(kb0);
+    issue(IntC<0>(), kb0, btv);
+    if (ntiles > 1) btv = fetch_bt(kb0 + kKT);
     auto step = [&](auto b, int t) {
       constexpr int B = decltype(b)::value;
-      const int kb = t * kKT;
+      const int kb = kb0 + t * kKT;
       wait_vmem<0>();                            // this thread's part of tile t (and the next table entries) landed
       lds_barrier();                             // all of tile t visible; buffer (t+1) % 2 no longer read
       if (t + 1 < ntiles) {
@@ -418,16 +439,16 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
     // E4M3: tile t + 1 is loaded into registers during step t and written to LDS after
     // tile t's products; the barrier that opens step t + 1 makes it visible.
     (void)issue;
-    int btv = fetch_bt(0);
+    int btv = fetch_bt(kb0);
     {
       u32x4 kr[NLD], vr[NLD];
-      load_regs(0, btv, kr, vr);
+      load_regs(kb0, btv, kr, vr);
       store_lds(IntC<0>(), kr, vr);
     }
-    if (ntiles > 1) btv = fetch_bt(kKT);
+    if (ntiles > 1) btv = fetch_bt(kb0 + kKT);
     auto step = [&](auto b, int t) {
       constexpr int B = decltype(b)::value;
-      const int kb = t * kKT;
+      const int kb = kb0 + t * kKT;
       wait_lds<0>();                             // this wave's writes of tile t are done
       lds_barrier();                             // all of tile t visible; buffer (t+1) % 2 no longer read
       const bool more = t + 1 < ntiles;
@@ -446,7 +467,67 @@ __global__ __launch_bounds__(kWavesP * kWave, 2) void prefill_kernel(AttnParams 
   // ---- finish: O / l, bf16 out; lane holds dims 32 dt + 8 q + 4 kg + 0..3 of its pair ----
   const int x = __float_as_int(l_part);
   const auto sw = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  const float l_tot = __int_as_float(sw[0]) + __int_as_float(sw[1]);
+  float l_tot = __int_as_float(sw[0]) + __int_as_float(sw[1]);
+  if (npieces > 1) {
+    // A piece of a split item: its partial (O against m_run, m_run, l) goes to the workspace
+    // rows of slot slot0 + piece, KV head h, written through to the device-coherent level
+    // (agent-scope stores), and the item's counter of this head is raised once they have
+    // landed.  The workgroup that raises it last reads every piece's partial the same way
+    // and writes O = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j, M = max_j m_j (the same
+    // rescale identity as the decode merge).  Every piece has at least 31 tiles and the last
+    // one starts below the item's first row, so every valid pair sees keys in every piece.
+    auto row_of = [&](int j) -> int64_t {
+      return ((int64_t)(slot0 + j) * p.Hkv + h) * kPrefillPairs + pair;
+    };
+    if (pvalid) {
+      float* po = p.ws_o + row_of(piece) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d = dt * 32 + 8 * q4 + 4 * kg;
+          store_coherent2(po + d, oacc[dt][q4 * 4 + 0], oacc[dt][q4 * 4 + 1]);
+          store_coherent2(po + d + 2, oacc[dt][q4 * 4 + 2], oacc[dt][q4 * 4 + 3]);
+        }
+      if (kg == 0) {
+        __hip_atomic_store(p.ws_m + row_of(piece), m_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p.ws_l + row_of(piece), l_tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    wait_vmem<0>();                              // this thread's partial has landed
+    __syncthreads();
+    __shared__ int last_piece;
+    if (threadIdx.x == 0)
+      last_piece = __hip_atomic_fetch_add(p.plan_split_ctr + (size_t)slot0 * p.Hkv + h, 1, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) == npieces - 1;
+    __syncthreads();
+    if (!last_piece || !pvalid) return;
+    float M = -INFINITY;
+    for (int j = 0; j < npieces; ++j)
+      M = fmaxf(M, __hip_atomic_load(p.ws_m + row_of(j), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
+    l_tot = 0.f;
+    for (int j = 0; j < npieces; ++j) {
+      const float mj = __hip_atomic_load(p.ws_m + row_of(j), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float wj = fast_exp2(mj - M);
+      l_tot += wj * __hip_atomic_load(p.ws_l + row_of(j), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const float* po = p.ws_o + row_of(j) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d = dt * 32 + 8 * q4 + 4 * kg;
+          const float2 a = load_coherent2(po + d), b2 = load_coherent2(po + d + 2);
+          oacc[dt][q4 * 4 + 0] += wj * a.x;
+          oacc[dt][q4 * 4 + 1] += wj * a.y;
+          oacc[dt][q4 * 4 + 2] += wj * b2.x;
+          oacc[dt][q4 * 4 + 3] += wj * b2.y;
+        }
+    }
+  }
   if (!pvalid) return;
   const float inv = F8 ? p.v_scale / l_tot : 1.f / l_tot;
   uint16_t* op = p.out + ((size_t)(row0 + jrow) * Hq + (size_t)h * G + gq) * D;

@@ -193,6 +193,9 @@ EDGE8 = [
     ("f8-multi-row-g4", [(700, 4), (5, 2), (1300, 3), (64, 4), (900, 1)], 16, 4, 128, 16),
     ("f8-short-and-long-chunks", [(800, 4), (1000, 300), (2000, 1), (90, 3), (513, 64)], 32, 8, 128, 16),
     ("f8-chunk-from-zero", [(512, 512), (97, 97)], 32, 8, 128, 16),
+    # a chunk over a long prefix: items cut into pieces of key tiles, partials merged
+    ("f8-split-long-prefix", [(20000 + 64, 64), (3000, 1)], 32, 8, 128, 16),
+    ("f8-split-d64-mha", [(12000 + 128, 128)], 8, 8, 64, 16),
 ]
 
 

@@ -152,6 +152,32 @@ def test_edge_shapes(name, specs, Hq, Hkv, D, bs):
     run_and_check(wl)
 
 
+# Chunks over long prefixes with few items for the device: the planner cuts each item of more
+# than 64 key tiles into pieces of consecutive tiles (one workgroup each, partials merged by the
+# last piece to finish).  Cases: pieces with d 128 / G 4, d 64 / G 1 (128-row items), G 16
+# (8-row items), a split item among short chunk items and decode rows, and a batch whose first
+# split length would need more partial slots than the workspace holds (the length is doubled,
+# every item still cut in two; rows sampled, the oracle being slow at that size).
+SPLIT = [
+    ("split-long-prefix", [(20000 + 64, 64), (3000, 1), (500, 1)], 32, 8, 128, 16, None),
+    ("split-d64-mha", [(12000 + 128, 128), (700, 1)], 8, 8, 64, 16, None),
+    ("split-g16", [(9000 + 40, 40)], 16, 1, 128, 16, None),
+    ("split-among-short-items", [(40000 + 100, 100), (600, 300), (200, 200), (5000, 1), (70, 1)],
+     32, 8, 128, 16, None),
+    ("split-length-doubled", [(8600 + 128, 128)] * 30, 8, 8, 64, 16, 48),
+]
+
+
+@pytest.mark.parametrize("name,specs,Hq,Hkv,D,bs,nrows", SPLIT, ids=[e[0] for e in SPLIT])
+def test_prefill_split_items(name, specs, Hq, Hkv, D, bs, nrows):
+    wl = W.custom(name, specs, Hq, Hkv, D, bs, seed=len(name) + 100)
+    rows = None
+    if nrows is not None:
+        rows = np.unique(np.random.default_rng(5).integers(0, wl.num_q_tokens, size=nrows))
+    print(f"{name}: {wl.num_q_tokens} rows, checking {len(rows) if rows is not None else 'all'}", flush=True)
+    run_and_check(wl, rows=rows)
+
+
 @pytest.mark.parametrize("scale", [-0.2, 0.0, 0.75], ids=["negative", "zero", "large"])
 def test_any_finite_softmax_scale(scale):
     """The softmax scale is any finite float: negative (the prefill kernel negates the
