@@ -244,6 +244,23 @@ def prefill_report(pkv, d, stream, torch):
                                  "(empty) decode grid and the merge launch that carries the planner"}}
 
 
+def long_prefix_report(pkv, dev, torch, stream):
+    """One 512-row chunk over a 65536-token cached prefix with the mixed batch's heads (Hq 32,
+    Hkv 8, d 128): 16 row tiles per KV head, too few for the device, so the planner cuts them
+    along the keys.  Timed like the prefill rows of the mixed batch."""
+    import workloads
+    wl = workloads.custom("long-prefix-chunk", [(65536 + 512, 512)], 32, 8, 128, 16, seed=31)
+    d = Device(wl, dev, torch)
+    pkv.kv_append(d.t["k_new"], d.t["v_new"], d.t["slots"], d.t["kc"], d.t["vc"], stream=stream)
+    torch.cuda.synchronize()
+    rec = prefill_report(pkv, d, stream, torch)
+    rec["roofline"]["note"] = ("flops = 4 d Hq x causal (row, key) pairs; 16 items per KV head cut into pieces "
+                               "of consecutive key tiles, merged by the last piece of each item")
+    del d
+    torch.cuda.empty_cache()
+    return rec
+
+
 def append_report(pkv, dev, torch, stream):
     """kv_append alone into a scratch pool: T new tokens of 8 KV heads x d 128 to random distinct slots."""
     Hkv, D, bs = 8, 128, 16
@@ -612,6 +629,8 @@ def config_record(cfg, args, torch, pkv, dev, stream, headline=False):
         rec["fp8"] = fp8_report(pkv, base, torch, stream, rec["roofline"]["avg_call_us"])
         if len(pre) and cfg != 0:
             rec["prefill_only"]["fp8"] = prefill_fp8_report(pkv, base, torch, stream)
+            log(f"config {cfg}: a chunk over a long prefix ...")
+            rec["prefill_only"]["long_prefix_chunk"] = long_prefix_report(pkv, dev, torch, stream)
     del copies, base
     torch.cuda.empty_cache()
     if not args.no_cpu:

@@ -62,6 +62,9 @@ FUSED_EDGE = [
     ("multi-row-g4", [(700, 4), (5, 2), (1300, 3), (64, 4), (2, 2), (900, 1)], 16, 4, 128, 16),
     ("block-boundary", [(16, 1), (17, 1), (64, 1), (65, 1), (32, 2), (80, 16)], 8, 8, 128, 16),
     ("long-many-pieces", [(100000, 1), (3, 1)], 8, 2, 128, 16),
+    # a chunk over a long prefix: its items cut into pieces (partials in the decode rows'
+    # workspace, after the merge launch has consumed them), decode rows beside it
+    ("split-prefill", [(20000 + 64, 64), (3000, 1), (700, 1)], 32, 8, 128, 16),
 ]
 
 

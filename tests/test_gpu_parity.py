@@ -473,7 +473,7 @@ def test_one_workspace_serves_calls_of_any_shape(gpu):
             compare(to_host_bits(db.out), ref, label=f"shared-ws-{wl.name}")
 
 
-@pytest.mark.parametrize("cfg", [0, 1, "share", 3])
+@pytest.mark.parametrize("cfg", [0, 1, "share", 3, "split"])
 def test_step_captured_in_hip_graph(gpu, cfg):
     """append + attention captured once in a HIP graph (the library allocates, memsets and
     synchronises nothing inside a call), replayed with new queries written in between by
@@ -482,9 +482,12 @@ def test_step_captured_in_hip_graph(gpu, cfg):
     import paged_kv_cache_tables_amd as pkv
     print(f"graph capture config {cfg}", flush=True)
     # config 3 and "share": decode rows in sharing groups (found from the tables in every
-    # replay), config 3 also prefill rows and the planner
+    # replay), config 3 also prefill rows and the planner; "split": a chunk over a long prefix,
+    # its items cut into pieces whose counters the planner clears in every replay
     wl = {0: lambda: W.config0(), 1: lambda: W.config1(num_seqs=16), 3: lambda: W.config3(),
-          "share": lambda: _share_case("share-two-groups-g4")}[cfg]()
+          "share": lambda: _share_case("share-two-groups-g4"),
+          "split": lambda: W.custom("graph-split", [(20000 + 64, 64), (3000, 1), (500, 1)], 32, 8, 128, 16,
+                                    seed=21)}[cfg]()
     db = DeviceBatch(wl)
     need = pkv.workspace_bytes(wl.num_seqs, wl.num_q_heads, wl.num_kv_heads, wl.head_dim,
                                wl.max_blocks_per_seq, wl.block_size, wl.max_query_len)
