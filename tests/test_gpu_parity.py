@@ -155,9 +155,10 @@ def test_edge_shapes(name, specs, Hq, Hkv, D, bs):
 # Chunks over long prefixes with few items for the device: the planner cuts each item of more
 # than 64 key tiles into pieces of consecutive tiles (one workgroup each, partials merged by the
 # last piece to finish).  Cases: pieces with d 128 / G 4, d 64 / G 1 (128-row items), G 16
-# (8-row items), a split item among short chunk items and decode rows, and a batch whose first
+# (8-row items), a split item among short chunk items and decode rows, a batch whose first
 # split length would need more partial slots than the workspace holds (the length is doubled,
-# every item still cut in two; rows sampled, the oracle being slow at that size).
+# every item still cut in two; rows sampled, the oracle being slow at that size), and KV head
+# counts of 6 and 16 (partial slots per head 85 and 32).
 SPLIT = [
     ("split-long-prefix", [(20000 + 64, 64), (3000, 1), (500, 1)], 32, 8, 128, 16, None),
     ("split-d64-mha", [(12000 + 128, 128), (700, 1)], 8, 8, 64, 16, None),
@@ -165,6 +166,9 @@ SPLIT = [
     ("split-among-short-items", [(40000 + 100, 100), (600, 300), (200, 200), (5000, 1), (70, 1)],
      32, 8, 128, 16, None),
     ("split-length-doubled", [(8600 + 128, 128)] * 30, 8, 8, 64, 16, 48),
+    # KV head counts that do not divide the partial slots evenly, and 16 heads of G 1
+    ("split-hkv6-g2", [(15000 + 48, 48), (900, 1)], 12, 6, 128, 16, None),
+    ("split-hkv16-g1", [(30000 + 128, 128)], 16, 16, 64, 16, 40),
 ]
 
 
