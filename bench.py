@@ -676,8 +676,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the attention shards by "
-              "KV heads or sequences with no collective; see DESIGN.md). Run with --gpus 1.",
+        print("bench.py measures one GPU: the library has no multi-GPU path (the attention would "
+              "shard by KV heads or by sequences, with no collective). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 

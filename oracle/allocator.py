@@ -20,7 +20,7 @@ Sources (web pages; cited by title and section):
   [SPEED] "The KV cache: ...": fixed-size blocks allocated on demand, mapped
           through a per-request block table, shared copy-on-write.
 
-Readings where the pages are silent (listed in the design doc):
+Readings where the pages are silent:
   * Only whole blocks are cached and matched; a match keeps at least one prompt
     token uncached, so it covers at most floor((n_prompt - 1) / bs) blocks.
   * Fresh blocks are taken lowest id first.

@@ -12,7 +12,7 @@ Sources (web pages; cited by title and section):
   [TGI]   "Text Generation Inference: ..." -- "Production Pattern: KV Cache
           Math" (the FP8 row of the bytes-per-token table: one byte per value).
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
   * The 8-bit format is E4M3 in the encoding without infinities ("FN"): sign
     bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds
     the subnormals m * 2^-9; the all-ones pattern S.1111.111 is NaN; the

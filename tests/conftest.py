@@ -21,7 +21,8 @@ def golden_dir():
 def pytest_terminal_summary(terminalreporter, exitstatus, config):
     """Per-comparison parity statistics of the GPU tests (raw max and mean absolute error against
     the float64 oracle, the bf16 rounding floor of the reference), one JSON line each, so that the
-    session's log keeps them; also written to gpurun_out/parity_stats.jsonl when that folder exists."""
+    session's log keeps them; also written to $PKV_PARITY_STATS_DIR/parity_stats.jsonl when that
+    variable names a folder."""
     import json
     harness = sys.modules.get("gpu_harness")
     log = getattr(harness, "PARITY_LOG", None)
@@ -37,7 +38,7 @@ def pytest_terminal_summary(terminalreporter, exitstatus, config):
         f"PARITY-SUMMARY comparisons={len(log)} max_abs={worst['max_abs']:.4e} ({worst['label']}) "
         f"max_mean_abs={worst_mean['mean_abs']:.4e} ({worst_mean['label']}) "
         f"relaxed_elements={sum(r['n_relaxed'] for r in log)}")
-    out = os.path.join(ROOT, "gpurun_out")
-    if os.path.isdir(out):
+    out = os.environ.get("PKV_PARITY_STATS_DIR", "")
+    if out and os.path.isdir(out):
         with open(os.path.join(out, "parity_stats.jsonl"), "w") as f:
             f.write("\n".join(lines) + "\n")

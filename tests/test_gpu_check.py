@@ -138,5 +138,5 @@ def test_random_corruptions_match_the_host_check():
             elif kind == 4:
                 k = int(rng.integers(1, S + 1))
                 m["qsl"][k] = max(0, int(m["qsl"][k]) + int(rng.integers(-2, 3)))
-        # the checker reads slot_mapping rows qsl[s] + j only inside [0, T)
+        # the metadata check reads slot_mapping rows qsl[s] + j only inside [0, T)
         assert device_flags(m) == host_flags(m), trial

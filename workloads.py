@@ -6,10 +6,10 @@ placements and N(0,1) values, rounds the draws to bf16 bit patterns, and lays
 the already-cached tokens into a block pool. Both the HIP library and the CPU
 oracle consume exactly the arrays it returns.
 
-Workload shapes follow the five configurations of the task (tiny mixed batch,
-Llama-3-8B-shaped decode, 70B-class decode, mixed batch with a shared prefix,
-long-context decode). The readings taken where the description is silent are
-stated next to each generator and collected in the design doc.
+Workload shapes: a tiny mixed batch, a Llama-3-8B-shaped decode batch, a
+70B-class decode batch, a mixed batch with a shared prefix and a long-context
+decode batch. The readings taken where the description is silent are stated
+next to each generator.
 
 Conventions
   * ``seq_lens[s]`` counts the tokens of sequence s *after* this step's
