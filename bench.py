@@ -673,6 +673,9 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the step, run a plain device copy of MIB MiB --steps times "
                          "(reference kernel for scaling rocprofv3 FETCH_SIZE/WRITE_SIZE)")
+    ap.add_argument("--long-prefix-only", action="store_true",
+                    help="instead of the step, time only the prefill call of one 512-row chunk over a "
+                         "65536-token cached prefix (its items cut along the keys) and print its record")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -701,6 +704,9 @@ def main():
     if args.kv == "fp8":
         args.no_extras = True
     stream = torch.cuda.current_stream(dev)
+    if args.long_prefix_only:
+        print(json.dumps({"long_prefix_chunk": long_prefix_report(pkv, dev, torch, stream)}), flush=True)
+        return
 
     head = config_record(args.config, args, torch, pkv, dev, stream, headline=True)
     fp8 = args.kv == "fp8"
