@@ -143,6 +143,11 @@ EDGE = [
     ("multi-row-mha", [(1500, 16), (16, 16), (40, 7)], 4, 4, 128, 16),
     ("spec-verify-long", [(20000 + 997 * i, 4) for i in range(6)], 32, 8, 128, 16),
     ("short-and-long-chunks", [(800, 4), (1000, 300), (2000, 1), (90, 3), (513, 64)], 32, 8, 128, 16),
+    # the planner lists up to 256 sequences with chunk rows and hands their items out one per
+    # thread; exactly 256 of them among decode rows, and 300 (one thread per sequence)
+    ("prefill-chunks-256", [(50 + (i * 41) % 300, 3 if i % 5 == 0 else 20) for i in range(320)],
+     8, 2, 128, 16),
+    ("prefill-chunks-300", [(30 + (i * 67) % 400, 17 + i % 16) for i in range(300)], 8, 2, 128, 16),
 ]
 
 
@@ -158,7 +163,8 @@ def test_edge_shapes(name, specs, Hq, Hkv, D, bs):
 # (8-row items), a split item among short chunk items and decode rows, a batch whose first
 # split length would need more partial slots than the workspace holds (the length is doubled,
 # every item still cut in two; rows sampled, the oracle being slow at that size), and KV head
-# counts of 6 and 16 (partial slots per head 85 and 32).
+# counts of 6 and 16 (partial slots per head 85 and 32), and a split item among more chunks
+# than the planner's sequence list holds.
 SPLIT = [
     ("split-long-prefix", [(20000 + 64, 64), (3000, 1), (500, 1)], 32, 8, 128, 16, None),
     ("split-d64-mha", [(12000 + 128, 128), (700, 1)], 8, 8, 64, 16, None),
@@ -169,6 +175,8 @@ SPLIT = [
     # KV head counts that do not divide the partial slots evenly, and 16 heads of G 1
     ("split-hkv6-g2", [(15000 + 48, 48), (900, 1)], 12, 6, 128, 16, None),
     ("split-hkv16-g1", [(30000 + 128, 128)], 16, 16, 64, 16, 40),
+    ("split-among-260-chunks", [(9000 + 5, 5)] + [(40 + (i * 53) % 300, 5) for i in range(260)],
+     16, 1, 128, 16, None),
 ]
 
 
