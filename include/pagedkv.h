@@ -386,7 +386,11 @@ PKV_API int pkv_allocator_allocate(pkv_allocator* a, const int32_t* tokens, int3
                            int32_t n_total, int64_t* alloc_id, int32_t* blocks, int32_t capacity,
                            int32_t* n_blocks, int32_t* prefix_len);
 
-/* End an allocation whose K/V now holds tokens[0..n_tokens); its whole blocks are cached. */
+/* End an allocation whose K/V now holds tokens[0..n_tokens); its whole blocks are cached.
+ * The tokens must be what the blocks hold: a block shared through fork holds the same tokens
+ * for every holder (writes go through prepare_write).  Tokens that contradict a shared block's
+ * content cache that block under a second prefix (it then counts twice in num_cached; it is
+ * still not handed out while any prefix or allocation holds it). */
 PKV_API int pkv_allocator_free(pkv_allocator* a, int64_t alloc_id, const int32_t* tokens,
                        int32_t n_tokens);
 
