@@ -17,10 +17,6 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 constexpr int kWave = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// bf16 halves of a packed dword, widened exactly to fp32.
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
 // Two fp32 values rounded to the nearest bf16 (ties to even) and packed, lo in the low
 // half (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -133,16 +129,7 @@ __device__ __forceinline__ float wave_reduce_dpp(float v, Op op) {
 }
 
 struct MaxOp { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
-struct SumOp { __device__ float operator()(float a, float b) const { return a + b; } };
 
 __device__ __forceinline__ float wave_max(float v) { return wave_reduce_dpp(v, MaxOp()); }
-__device__ __forceinline__ float wave_sum(float v) { return wave_reduce_dpp(v, SumOp()); }
-
-// v[lane % 32] + v[32 + lane % 32] in every lane (the two half-waves added).
-__device__ __forceinline__ float half_wave_sum(float v) {
-  const int x = __float_as_int(v);
-  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  return __int_as_float(r[0]) + __int_as_float(r[1]);
-}
 
 }  // namespace pkv
