@@ -163,8 +163,8 @@ def test_edge_shapes(name, specs, Hq, Hkv, D, bs):
 # (8-row items), a split item among short chunk items and decode rows, a batch whose first
 # split length would need more partial slots than the workspace holds (the length is doubled,
 # every item still cut in two; rows sampled, the oracle being slow at that size), and KV head
-# counts of 6 and 16 (partial slots per head 85 and 32), and a split item among more chunks
-# than the planner's sequence list holds.
+# counts of 6 and 16 (partial slots per head 85 and 32), a split item among more chunks than
+# the planner's sequence list holds, and block sizes 8 and 32.
 SPLIT = [
     ("split-long-prefix", [(20000 + 64, 64), (3000, 1), (500, 1)], 32, 8, 128, 16, None),
     ("split-d64-mha", [(12000 + 128, 128), (700, 1)], 8, 8, 64, 16, None),
@@ -177,6 +177,9 @@ SPLIT = [
     ("split-hkv16-g1", [(30000 + 128, 128)], 16, 16, 64, 16, 40),
     ("split-among-260-chunks", [(9000 + 5, 5)] + [(40 + (i * 53) % 300, 5) for i in range(260)],
      16, 1, 128, 16, None),
+    # pool blocks of 8 and 32 tokens (a piece starts on a 64-key tile, so on a block boundary)
+    ("split-bs8", [(9000 + 64, 64), (300, 1)], 32, 8, 128, 8, None),
+    ("split-bs32-d64", [(12000 + 100, 100), (77, 1)], 16, 4, 64, 32, None),
 ]
 
 
