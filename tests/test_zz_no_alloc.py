@@ -54,6 +54,24 @@ def test_noalloc_equals_workspace_call_twice_shrinking(gpu):
         assert np.array_equal(to_host_bits(got.out), to_host_bits(ref.out)), "output differs"
 
 
+def test_noalloc_split_prefill_twice(gpu):
+    """Chunks over long prefixes whose items are cut into pieces: the pieces' partials and the
+    per-item counters that find the last piece live in the scratch too, and the planner clears
+    the counters it uses on every call (the second call reuses slots the first one raised)."""
+    torch = gpu
+    import paged_kv_cache_tables_amd as pkv
+    cases = [W.custom("noalloc-split-a", [(20000 + 64, 64), (3000, 1), (500, 1)], 32, 8, 128, 16, seed=11),
+             W.custom("noalloc-split-b", [(9000 + 40, 40)], 32, 8, 128, 16, seed=12)]
+    for i, wl in enumerate(cases):
+        print(f"noalloc split call {i}: {wl.name}, {wl.num_q_tokens} rows", flush=True)
+        ref, got = _pair(wl)
+        _fused(pkv, ref, noalloc=False)
+        _fused(pkv, got, noalloc=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host_bits(got.k_cache), to_host_bits(ref.k_cache)), "K pool differs"
+        assert np.array_equal(to_host_bits(got.out), to_host_bits(ref.out)), "output differs"
+
+
 def test_noalloc_long_context_and_too_large_shape(gpu):
     torch = gpu
     import paged_kv_cache_tables_amd as pkv
